@@ -1,0 +1,213 @@
+"""Seeded synthetic workloads for causal NeoX-rotary attention.
+
+This module only *generates inputs*: shapes, seeded normal draws, rounding of
+those draws to the storage type, and the packed-document layout.  It holds none
+of the attention arithmetic, so the CPU oracle and the HIP path can both be fed
+from it without sharing any of the method.
+
+Shapes follow the GPT-NeoX pages:
+  * context length 2048 ("GPT-NeoX: Как 20-миллиардная модель от EleutherAI
+    изменила открытый ИИ", section "Ключевые особенности и архитектура");
+  * the 20B head layout, 64 heads x 96 dims with 24 rotary dims
+    ("FasterTransformer GPT-NeoX 推理指南", section "模型配置", config.ini fields
+    head_num / size_per_head / rotary_embedding);
+  * RoPE and ALiBi as the two position schemes ("GPT-NeoX 开源训练框架深度解读",
+    section "架构创新").
+
+Recipe (every workload): numpy ``SeedSequence(seed).spawn(5)`` gives independent
+streams for q, k, v, dO and the document lengths; q, k, v, dO are N(0, 1) draws
+in float64, multiplied by ``amp``, cast to float32 and, for bf16 workloads,
+rounded to bfloat16 with round-to-nearest-even.  Document lengths are drawn per
+batch row from that row's own child stream.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention problem: sizes, position scheme and input recipe."""
+
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    rotary_dim: int
+    dtype: str  # "bf16" or "f32": storage type of q, k, v, o, dO
+    backward: bool = True
+    rope_base: float = 10000.0
+    causal: bool = True
+    alibi: bool = False
+    packed_docs: bool = False
+    doc_min: int = 64
+    doc_max: int = 4096
+    amp: float = 1.0
+    seed: int = 20260000
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def with_sizes(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the library is measured and checked on, plus the S=2048,
+# D=128 shape used for the forward-efficiency figure.  Seeds are 20260000 + the
+# workload's index (1-based for the five, 6 for the D=128 shape).
+WORKLOADS = {
+    "fp32_s128_d64": Workload(
+        "fp32_s128_d64", B=1, H=2, S=128, D=64, rotary_dim=64, dtype=F32,
+        backward=False, seed=20260001),
+    "bf16_s2048_d64_rd16": Workload(
+        "bf16_s2048_d64_rd16", B=8, H=12, S=2048, D=64, rotary_dim=16,
+        dtype=BF16, seed=20260002),
+    "neox20b_s2048_h64_d96_rd24": Workload(
+        "neox20b_s2048_h64_d96_rd24", B=4, H=64, S=2048, D=96, rotary_dim=24,
+        dtype=BF16, seed=20260003),
+    "long_s16384_d128": Workload(
+        "long_s16384_d128", B=1, H=32, S=16384, D=128, rotary_dim=128,
+        dtype=BF16, amp=0.5, seed=20260004),
+    "alibi_docs_s4096_d128": Workload(
+        "alibi_docs_s4096_d128", B=4, H=32, S=4096, D=128, rotary_dim=0,
+        dtype=BF16, alibi=True, packed_docs=True, seed=20260005),
+    "rope_s2048_d128": Workload(
+        "rope_s2048_d128", B=4, H=32, S=2048, D=128, rotary_dim=128,
+        dtype=BF16, seed=20260006),
+}
+
+# Workload whose fwd+bwd throughput is the headline figure: the 2048-token
+# context with the 20B head layout.
+BENCH_WORKLOAD = "neox20b_s2048_h64_d96_rd24"
+# Shape for the causal-forward efficiency figure (S=2048, D=128).
+FWD_TARGET_WORKLOAD = "rope_s2048_d128"
+
+
+def round_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    NaN is not expected in generated data; infinities stay infinities.
+    """
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = (u + 0x7FFF + lsb) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exactly equal float32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Generated tensors of one workload.
+
+    ``q, k, v, dout`` are the storage values: uint16 bf16 bit patterns for bf16
+    workloads, float32 for f32 workloads, shaped [B, H, S, D].  ``doc_offsets``
+    is int32 [B, n_docs_max + 1] (0 first, S last, non-decreasing; rows with
+    fewer documents repeat S), or None for one document per row.
+    """
+
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dout: Optional[np.ndarray]
+    doc_offsets: Optional[np.ndarray]
+
+    def as_f64(self, name: str) -> np.ndarray:
+        """A generated tensor widened exactly to float64."""
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if self.wl.dtype == BF16:
+            return bf16_bits_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def pack_documents(rng: np.random.Generator, S: int, lo: int, hi: int) -> list:
+    """Document lengths for one batch row: draws L ~ UniformInt[lo, hi]
+    (inclusive) until the row is full; when the room left after a draw would be
+    shorter than ``lo`` the draw is replaced by all the room left, so every
+    length lies in [lo, hi] (or is S itself when S < lo) and they sum to S."""
+    lengths = []
+    remaining = S
+    while remaining > 0:
+        L = int(rng.integers(lo, hi + 1))
+        if remaining - L < lo:
+            L = remaining
+        lengths.append(L)
+        remaining -= L
+    return lengths
+
+
+def doc_offsets_from_lengths(rows: list, S: int) -> np.ndarray:
+    """Per-row lengths -> int32 [B, n_max + 1] cumulative offsets padded with S."""
+    n_max = max(len(r) for r in rows)
+    out = np.full((len(rows), n_max + 1), S, dtype=np.int32)
+    for b, lengths in enumerate(rows):
+        out[b, 0] = 0
+        out[b, 1:len(lengths) + 1] = np.cumsum(lengths)
+    return out
+
+
+def _draw(rng: np.random.Generator, shape, amp: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float64)
+    if amp != 1.0:
+        x *= amp
+    x32 = x.astype(np.float32)
+    if dtype == BF16:
+        return round_to_bf16_bits(x32)
+    return x32
+
+
+def generate(wl: Workload, with_dout: Optional[bool] = None) -> Inputs:
+    """Seeded inputs of ``wl`` (see the module docstring for the recipe)."""
+    if with_dout is None:
+        with_dout = wl.backward
+    ss_q, ss_k, ss_v, ss_do, ss_docs = np.random.SeedSequence(wl.seed).spawn(5)
+    shape = (wl.B, wl.H, wl.S, wl.D)
+    q = _draw(np.random.default_rng(ss_q), shape, wl.amp, wl.dtype)
+    k = _draw(np.random.default_rng(ss_k), shape, wl.amp, wl.dtype)
+    v = _draw(np.random.default_rng(ss_v), shape, wl.amp, wl.dtype)
+    dout = _draw(np.random.default_rng(ss_do), shape, wl.amp, wl.dtype) if with_dout else None
+    docs = None
+    if wl.packed_docs:
+        rows = [pack_documents(np.random.default_rng(s), wl.S, wl.doc_min, wl.doc_max)
+                for s in ss_docs.spawn(wl.B)]
+        docs = doc_offsets_from_lengths(rows, wl.S)
+    return Inputs(wl, q, k, v, dout, docs)
+
+
+
+def allowed_pairs(S: int, causal: bool = True, doc_offsets_row=None) -> int:
+    """Count of (query, key) pairs one head attends over: the unit of
+    algorithmic work.  Causal: L(L+1)/2 per document of length L; otherwise L^2.
+    """
+    if doc_offsets_row is None:
+        lengths = [S]
+    else:
+        off = np.asarray(doc_offsets_row, dtype=np.int64)
+        lengths = [int(x) for x in np.diff(off) if x > 0]
+    if causal:
+        return sum(L * (L + 1) // 2 for L in lengths)
+    return sum(L * L for L in lengths)
+
+
+def total_pairs(inp: "Inputs") -> int:
+    """Allowed pairs summed over all B x H heads of generated inputs."""
+    wl = inp.wl
+    if inp.doc_offsets is None:
+        return wl.B * wl.H * allowed_pairs(wl.S, wl.causal)
+    return wl.H * sum(allowed_pairs(wl.S, wl.causal, row) for row in inp.doc_offsets)

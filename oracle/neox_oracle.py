@@ -1,0 +1,277 @@
+"""Plain double-precision CPU oracle for causal NeoX-rotary attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is imported only by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``.
+The library (``causal_attention_neox_amd``) never imports, calls or links it, and
+it imports nothing from the library: the two share no code.
+
+What it computes, and where that comes from:
+
+* The attention is exact: the GPT-NeoX pages say FlashAttention-2 is an exact
+  attention algorithm that leaves the mathematical result unchanged and only
+  changes tiling and IO ("GPT-NeoX 开源训练框架深度解读", section
+  "问题二：注意力计算太慢").  So the oracle is the plain definition: the full
+  score matrix of each head, a row-wise softmax, and the matrix products, with
+  no tiling and no online rescaling.
+* Rotary position embedding in the NeoX style is applied to both queries and
+  keys ("FasterTransformer GPT-NeoX 推理指南", the GptNeoX.h facts
+  ``neox_rotary_style_ true`` and section "模型配置": ``rotary_embedding 24``
+  of ``size_per_head 96``, Q and K both rotated).  Only the first
+  ``rotary_dim`` dims rotate; the frequencies are one per rotary pair, the
+  ``attention.rotary_emb.inv_freq`` buffer of the same page's checkpoint list.
+* ALiBi is the alternative position scheme ("GPT-NeoX 开源训练框架深度解读",
+  section "架构创新").
+* Autoregressive language modelling means causal attention (GPT-NeoX tool page,
+  first paragraph; "GPT-NeoX: Как 20-миллиардная модель", section
+  "Ключевые особенности и архитектура").
+
+Readings taken where the pages are silent (each is also listed with the design
+notes of this repository):
+  R1  rotate-half pairing: dim p pairs with p + rotary_dim/2 (not GPT-J's
+      interleaved 2p, 2p+1);
+  R2  rotation sign: y_p = x_p cos - x_{p+h} sin, y_{p+h} = x_{p+h} cos + x_p sin,
+      i.e. multiplication of (x_p + i x_{p+h}) by exp(+i theta);
+  R3  theta[t, p] = t * base^(-2p / rotary_dim): the frequency denominator is
+      rotary_dim, positions are 0..S-1 in each batch row;
+  R4  scores s_ij = scale * (q~_i . k~_j) + bias_ij, the ALiBi bias added after
+      scaling and not scaled; bias_ij = -slope_h * (i - j);
+  R5  ALiBi slope of head h (0-based) is 2^(-8 (h+1) / H);
+  R6  allowed(i, j) <=> (not causal or j <= i) and doc(i) == doc(j); the
+      diagonal is allowed, so every row has at least one key;
+  R7  lse is the natural-log logsumexp of the allowed scores of a row.
+
+Pins (tests that fix this oracle to something other than itself) live in
+``tests/test_oracle_pins.py``: torch's float64 scaled_dot_product_attention and
+autograd as a library special case, central finite differences, the complex
+multiplication form of the rotation, closed forms (S=1, q=0 prefix means, the
+ALiBi geometric mean, v constant), invariants (rows of P sum to 1, rotation
+preserves norms, relative-position property, gradient sums per document) and
+the page's 20B head layout.  R1, R2 and R5 are readings the pages do not fix:
+the tests pin the oracle to them, not to the pages ("parity unpinned" against
+the pages for the rotation convention and the slope schedule).
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding
+# --------------------------------------------------------------------------
+
+def rope_inv_freq(rotary_dim: int, base: float) -> np.ndarray:
+    """Frequencies base^(-2p / rotary_dim) for p = 0 .. rotary_dim/2 - 1 (R3)."""
+    if rotary_dim % 2:
+        raise ValueError("rotary_dim must be even")
+    p = np.arange(rotary_dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * p / rotary_dim)
+
+
+def rope_angles(positions: np.ndarray, rotary_dim: int, base: float) -> np.ndarray:
+    """theta[t, p] = positions[t] * inv_freq[p]  (shape [len(positions), rd/2])."""
+    pos = np.asarray(positions, dtype=np.float64)
+    return np.multiply.outer(pos, rope_inv_freq(rotary_dim, base))
+
+
+def rope_rotate(x: np.ndarray, positions: np.ndarray, rotary_dim: int, base: float,
+                inverse: bool = False) -> np.ndarray:
+    """NeoX rotate-half rotation of the first ``rotary_dim`` dims of x (R1, R2).
+
+    ``x`` is [..., S, D] and ``positions`` has length S.  With ``inverse`` the
+    rotation is by -theta (the transpose R^T), which maps a gradient with
+    respect to the rotated vector back to the unrotated one.  Dims at or beyond
+    ``rotary_dim`` pass through unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rd = int(rotary_dim)
+    if rd == 0:
+        return x.copy()
+    half = rd // 2
+    theta = rope_angles(positions, rd, base)
+    if inverse:
+        theta = -theta
+    c = np.cos(theta)
+    s = np.sin(theta)
+    x1 = x[..., :half]
+    x2 = x[..., half:rd]
+    y = x.copy()
+    y[..., :half] = x1 * c - x2 * s
+    y[..., half:rd] = x2 * c + x1 * s
+    return y
+
+
+# --------------------------------------------------------------------------
+# Masks and biases
+# --------------------------------------------------------------------------
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """Slope of head h: 2^(-8 (h+1) / H), h = 0 .. H-1 (R5)."""
+    h = np.arange(H, dtype=np.float64)
+    return np.power(2.0, -8.0 * (h + 1.0) / H)
+
+
+def doc_index(offsets_row: Optional[np.ndarray], S: int) -> np.ndarray:
+    """doc(t) for t = 0..S-1: the d with offsets[d] <= t < offsets[d+1].
+
+    ``offsets_row`` starts at 0, never decreases and ends at S; empty documents
+    (equal neighbours) own no token.  None means a single document.
+    """
+    if offsets_row is None:
+        return np.zeros(S, dtype=np.int64)
+    off = np.asarray(offsets_row, dtype=np.int64)
+    t = np.arange(S)
+    # number of offsets <= t, minus one: the last d with offsets[d] <= t
+    return np.searchsorted(off, t, side="right") - 1
+
+
+def allowed_mask(S: int, causal: bool, offsets_row: Optional[np.ndarray]) -> np.ndarray:
+    """Boolean [S, S]: allowed[i, j] (R6)."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    ok = np.ones((S, S), dtype=bool)
+    if causal:
+        ok &= j <= i
+    d = doc_index(offsets_row, S)
+    ok &= d[:, None] == d[None, :]
+    return ok
+
+
+def alibi_bias(S: int, slope: float) -> np.ndarray:
+    """bias[i, j] = -slope * (i - j)  (R4)."""
+    i = np.arange(S, dtype=np.float64)[:, None]
+    j = np.arange(S, dtype=np.float64)[None, :]
+    return -float(slope) * (i - j)
+
+
+# --------------------------------------------------------------------------
+# One head: forward and backward by the definition
+# --------------------------------------------------------------------------
+
+def _head_probs(qr, kr, scale, bias, allowed):
+    """Scores of one head, then P = exp(s - lse) row by row (two passes)."""
+    s = scale * (qr @ kr.T)
+    if bias is not None:
+        s += bias
+    s[~allowed] = -np.inf
+    m = s.max(axis=1)                       # row max over allowed keys
+    s -= m[:, None]
+    np.exp(s, out=s)                        # masked entries become exactly 0
+    l = s.sum(axis=1)
+    lse = m + np.log(l)
+    s /= l[:, None]                         # s now holds P
+    return s, lse
+
+
+def head_forward(q, k, v, *, rotary_dim, rope_base, causal, scale, slope=None,
+                 offsets_row=None):
+    """o [S, D] and lse [S] of one head."""
+    S = q.shape[0]
+    pos = np.arange(S)
+    qr = rope_rotate(q, pos, rotary_dim, rope_base)
+    kr = rope_rotate(k, pos, rotary_dim, rope_base)
+    bias = alibi_bias(S, slope) if slope is not None else None
+    P, lse = _head_probs(qr, kr, scale, bias, allowed_mask(S, causal, offsets_row))
+    o = P @ v
+    return o, lse
+
+
+def head_backward(q, k, v, dout, *, rotary_dim, rope_base, causal, scale, slope=None,
+                  offsets_row=None):
+    """(o, lse, dq, dk, dv) of one head, by differentiating the definition.
+
+    dv_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  Delta_i = dO_i . o_i;
+    dS_ij = P_ij (dP_ij - Delta_i);  dq~_i = scale sum_j dS_ij k~_j;
+    dk~_j = scale sum_i dS_ij q~_i;  dq = R^T dq~,  dk = R^T dk~.
+    The bias does not depend on q, k, v, so it adds no gradient term.
+    """
+    S = q.shape[0]
+    pos = np.arange(S)
+    qr = rope_rotate(q, pos, rotary_dim, rope_base)
+    kr = rope_rotate(k, pos, rotary_dim, rope_base)
+    bias = alibi_bias(S, slope) if slope is not None else None
+    P, lse = _head_probs(qr, kr, scale, bias, allowed_mask(S, causal, offsets_row))
+    o = P @ v
+    dv = P.T @ dout
+    dP = dout @ v.T
+    delta = np.sum(dout * o, axis=1)
+    dS = P * (dP - delta[:, None])
+    dqr = scale * (dS @ kr)
+    dkr = scale * (dS.T @ qr)
+    dq = rope_rotate(dqr, pos, rotary_dim, rope_base, inverse=True)
+    dk = rope_rotate(dkr, pos, rotary_dim, rope_base, inverse=True)
+    return o, lse, dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# Batched front ends ([B, H, S, D] float64 arrays)
+# --------------------------------------------------------------------------
+
+def _heads(B: int, H: int, heads: Optional[Iterable[Tuple[int, int]]]):
+    if heads is None:
+        return [(b, h) for b in range(B) for h in range(H)]
+    return [(int(b), int(h)) for b, h in heads]
+
+
+def _slopes(H, alibi):
+    if alibi is None or alibi is False:
+        return None
+    if alibi is True:
+        return alibi_slopes(H)
+    return np.asarray(alibi, dtype=np.float64)
+
+
+def attn_fwd(q, k, v, *, rotary_dim: int, rope_base: float = 10000.0, causal: bool = True,
+             softmax_scale: Optional[float] = None, alibi=False,
+             doc_offsets: Optional[np.ndarray] = None,
+             heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Forward of attention over [B, H, S, D] float64 inputs.
+
+    ``alibi`` is False, True (slopes by R5) or an explicit [H] slope array.
+    ``heads`` restricts the work to a list of (b, h); the results are then
+    stacked in that order as o [n, S, D] and lse [n, S].  Heads are independent,
+    so a restricted run gives exactly the full run's values for those heads.
+    """
+    B, H, S, D = q.shape
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    slopes = _slopes(H, alibi)
+    hl = _heads(B, H, heads)
+    o = np.empty((len(hl), S, D))
+    lse = np.empty((len(hl), S))
+    for n, (b, h) in enumerate(hl):
+        o[n], lse[n] = head_forward(
+            q[b, h], k[b, h], v[b, h], rotary_dim=rotary_dim, rope_base=rope_base,
+            causal=causal, scale=scale, slope=None if slopes is None else slopes[h],
+            offsets_row=None if doc_offsets is None else doc_offsets[b])
+    if heads is None:
+        return o.reshape(B, H, S, D), lse.reshape(B, H, S)
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, *, rotary_dim: int, rope_base: float = 10000.0,
+             causal: bool = True, softmax_scale: Optional[float] = None, alibi=False,
+             doc_offsets: Optional[np.ndarray] = None,
+             heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """(o, lse, dq, dk, dv) over [B, H, S, D] float64 inputs; see attn_fwd."""
+    B, H, S, D = q.shape
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    slopes = _slopes(H, alibi)
+    hl = _heads(B, H, heads)
+    out = [np.empty((len(hl), S, D)), np.empty((len(hl), S)), np.empty((len(hl), S, D)),
+           np.empty((len(hl), S, D)), np.empty((len(hl), S, D))]
+    for n, (b, h) in enumerate(hl):
+        res = head_backward(
+            q[b, h], k[b, h], v[b, h], dout[b, h], rotary_dim=rotary_dim,
+            rope_base=rope_base, causal=causal, scale=scale,
+            slope=None if slopes is None else slopes[h],
+            offsets_row=None if doc_offsets is None else doc_offsets[b])
+        for dst, r in zip(out, res):
+            dst[n] = r
+    if heads is None:
+        return (out[0].reshape(B, H, S, D), out[1].reshape(B, H, S),
+                out[2].reshape(B, H, S, D), out[3].reshape(B, H, S, D),
+                out[4].reshape(B, H, S, D))
+    return tuple(out)
+
