@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+// Parameter blocks are passed by value to the kernels; every pointer in them is
+// a device pointer.  Launchers return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace neox {
+
+// Element strides of one [B, H, S, D] tensor (head dim contiguous).
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct AttnShape {
+  int B, H, S, D;
+  int rd;                 // rotary dims (0 = none)
+  const float2* rope;     // [S][rd/2] (cos, sin) or null when rd == 0
+  float scale;            // softmax scale
+  float scale_log2;       // softmax scale * log2(e)
+  int causal;
+  int alibi;              // 1: add -slope*(i-j)
+  const float* slopes;    // [H] or null (then 2^(-8(h+1)/H))
+  const int32_t* docs;    // [B][n_docs+1] or null
+  int n_docs;
+};
+
+struct FwdParams {
+  AttnShape a;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  Strides sq, sk, sv, so;
+  int out_f32;  // o stored as fp32
+};
+
+struct BwdParams {
+  AttnShape a;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // [B][H][S][D] fp32 workspace (contiguous)
+  float* delta;   // [B][H][S] fp32 workspace
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int out_f32;    // dq, dk, dv stored as fp32
+};
+
+hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
+
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
+
+// `ev` is null or 4 events recorded before the preprocess kernel, after it,
+// after the main kernel(s) and after the dq finalize.
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
+
+// Preprocess (Delta, zeroed dq accumulator) and dq finalize, shared by both paths.
+hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t st, bool f32);
+hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32);
+
+inline hipError_t record_event(const hipEvent_t* ev, int i, hipStream_t st) {
+  return ev ? hipEventRecord(ev[i], st) : hipSuccess;
+}
+
+}  // namespace neox

@@ -1,0 +1,360 @@
+// Host side of libneoxattn: argument validation, kernel dispatch and the
+// per-device rotary cos/sin table cache.  Every exported function is declared
+// in include/neoxattn.h, which documents arguments, ownership and errors.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/neoxattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // B*H*S must stay below 2^31
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// ---------------------------------------------------------------- device check
+
+struct DeviceInfo {
+  bool checked = false;
+  bool ok = false;
+};
+
+std::mutex g_mu;
+std::vector<DeviceInfo> g_devices;
+
+int check_device(int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NEOX_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
+  DeviceInfo& info = g_devices[dev];
+  if (!info.checked) {
+    hipDeviceProp_t prop;
+    info.checked = true;
+    info.ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+              std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  }
+  *dev_out = dev;
+  return info.ok ? NEOX_OK : NEOX_E_DEVICE;
+}
+
+// ---------------------------------------------------------------- rotary tables
+
+struct RopeTable {
+  int dev;
+  int rd;
+  uint32_t base_bits;
+  int cap;  // positions 0..cap-1
+  float2* ptr;
+};
+
+std::vector<RopeTable> g_tables;  // never freed: kernels in flight may read them
+
+uint32_t float_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
+// Returns a table covering positions 0..S-1.  A new table is built on `st` and
+// waited for; under stream capture that is impossible, so the caller gets
+// NEOX_E_ALLOC and must call neox_rope_table_prepare() first.
+int get_rope_table(int dev, int S, int rd, float base, hipStream_t st, const float2** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const uint32_t bb = float_bits(base);
+  for (const RopeTable& t : g_tables) {
+    if (t.dev == dev && t.rd == rd && t.base_bits == bb && t.cap >= S) {
+      *out = t.ptr;
+      return NEOX_OK;
+    }
+  }
+  if (st != nullptr) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NEOX_E_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return NEOX_E_ALLOC;
+  }
+  int cap = S;
+  for (const RopeTable& t : g_tables)
+    if (t.dev == dev && t.rd == rd && t.base_bits == bb && 2 * t.cap > cap) cap = 2 * t.cap;
+  cap = (cap + 255) & ~255;
+  float2* ptr = nullptr;
+  if (hipMalloc(&ptr, (size_t)cap * (size_t)(rd / 2) * sizeof(float2)) != hipSuccess) {
+    (void)hipGetLastError();
+    return NEOX_E_ALLOC;
+  }
+  if (neox::launch_rope_table(ptr, cap, rd, (double)base, st) != hipSuccess) return NEOX_E_LAUNCH;
+  if (hipStreamSynchronize(st) != hipSuccess) return NEOX_E_DEVICE;
+  g_tables.push_back(RopeTable{dev, rd, bb, cap, ptr});
+  *out = ptr;
+  return NEOX_OK;
+}
+
+// ---------------------------------------------------------------- validation
+
+int validate_common(const neox_attn_args* a) {
+  if (!a) return NEOX_E_ARG;
+  if (a->B < 1 || a->H < 1 || a->S < 1 || a->D < 1) return NEOX_E_ARG;
+  if ((int64_t)a->B * a->H * a->S >= kMaxRows) return NEOX_E_ARG;
+  if (a->dtype != NEOX_F32 && a->dtype != NEOX_BF16) return NEOX_E_ARG;
+  if (a->pos != NEOX_POS_NONE && a->pos != NEOX_POS_ROPE && a->pos != NEOX_POS_ALIBI)
+    return NEOX_E_ARG;
+  if (!finite_pos(a->softmax_scale)) return NEOX_E_ARG;
+  if (a->out_dtype != NEOX_OUT_SAME && a->out_dtype != NEOX_OUT_F32) return NEOX_E_ARG;
+  if (a->pos == NEOX_POS_ROPE) {
+    if (a->rotary_dim < 0 || a->rotary_dim > a->D || (a->rotary_dim & 1)) return NEOX_E_ARG;
+    if (!finite_pos(a->rope_base)) return NEOX_E_ARG;
+  } else if (a->rotary_dim != 0) {
+    return NEOX_E_ARG;
+  }
+  if (a->alibi_slopes && a->pos != NEOX_POS_ALIBI) return NEOX_E_ARG;
+  if (a->doc_offsets) {
+    if (a->n_docs < 1 || a->n_docs > (1 << 24)) return NEOX_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(a->doc_offsets) & 3u) != 0) return NEOX_E_ALIGN;
+  } else if (a->n_docs != 0) {
+    return NEOX_E_ARG;
+  }
+  if (a->alibi_slopes && (reinterpret_cast<uintptr_t>(a->alibi_slopes) & 3u) != 0)
+    return NEOX_E_ALIGN;
+  if (a->D != 64 && a->D != 96 && a->D != 128) return NEOX_E_UNSUPPORTED;
+  return NEOX_OK;
+}
+
+// Checks one tensor: pointer present and 16-byte aligned, strides non-negative
+// and multiples of the 16-byte unit (`unit` elements).
+int check_tensor(const void* p, const neox_strides& s, int unit) {
+  if (!p) return NEOX_E_ARG;
+  if (s.batch < 0 || s.head < 0 || s.seq < 0) return NEOX_E_ARG;
+  if (!aligned16(p)) return NEOX_E_ALIGN;
+  if (s.batch % unit || s.head % unit || s.seq % unit) return NEOX_E_ALIGN;
+  return NEOX_OK;
+}
+
+neox_strides contiguous(const neox_attn_args* a) {
+  const int64_t sd = a->D;
+  return neox_strides{(int64_t)a->H * a->S * sd, (int64_t)a->S * sd, sd};
+}
+
+neox::Strides to_internal(const neox_strides& s) { return neox::Strides{s.batch, s.head, s.seq}; }
+
+int fill_shape(const neox_attn_args* a, const float2* rope, neox::AttnShape* sh) {
+  sh->B = a->B;
+  sh->H = a->H;
+  sh->S = a->S;
+  sh->D = a->D;
+  sh->rd = a->pos == NEOX_POS_ROPE ? a->rotary_dim : 0;
+  sh->rope = rope;
+  sh->scale = a->softmax_scale;
+  sh->scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  sh->causal = a->causal != 0;
+  sh->alibi = a->pos == NEOX_POS_ALIBI;
+  sh->slopes = a->alibi_slopes;
+  sh->docs = a->doc_offsets;
+  sh->n_docs = a->doc_offsets ? a->n_docs : 0;
+  return NEOX_OK;
+}
+
+int prepare_rope(const neox_attn_args* a, int dev, hipStream_t st, const float2** rope) {
+  *rope = nullptr;
+  if (a->pos == NEOX_POS_ROPE && a->rotary_dim > 0)
+    return get_rope_table(dev, a->S, a->rotary_dim, a->rope_base, st, rope);
+  return NEOX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* neox_status_str(int status) {
+  switch (status) {
+    case NEOX_OK: return "ok";
+    case NEOX_E_ARG: return "invalid argument";
+    case NEOX_E_UNSUPPORTED: return "unsupported configuration";
+    case NEOX_E_ALIGN: return "misaligned pointer or stride";
+    case NEOX_E_WORKSPACE: return "workspace missing or too small";
+    case NEOX_E_LAUNCH: return "kernel launch failed";
+    case NEOX_E_DEVICE: return "no usable gfx950 device or HIP runtime error";
+    case NEOX_E_ALLOC: return "rotary table allocation failed or not prepared under capture";
+    default: return "unknown status";
+  }
+}
+
+size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1 || D < 1) return 0;
+  const int64_t rows = (int64_t)B * H * S;
+  if (rows >= kMaxRows || D > 4096) return 0;
+  return round256((size_t)rows * (size_t)D * 4u) + round256((size_t)rows * 4u);
+}
+
+int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* stream) {
+  int st = validate_common(a);
+  if (st != NEOX_OK) return st;
+  const neox_strides def = contiguous(a);
+  const neox_strides* s = a->strides;
+  const int unit_in = a->dtype == NEOX_BF16 ? 8 : 4;
+  const int unit_out = (a->dtype == NEOX_BF16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
+  if ((st = check_tensor(q, s ? s[0] : def, unit_in)) != NEOX_OK) return st;
+  if ((st = check_tensor(k, s ? s[1] : def, unit_in)) != NEOX_OK) return st;
+  if ((st = check_tensor(v, s ? s[2] : def, unit_in)) != NEOX_OK) return st;
+  if ((st = check_tensor(o, s ? s[3] : def, unit_out)) != NEOX_OK) return st;
+  if (!lse) return NEOX_E_ARG;
+  if (!aligned16(lse)) return NEOX_E_ALIGN;
+
+  int dev = 0;
+  if ((st = check_device(&dev)) != NEOX_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const float2* rope = nullptr;
+  if ((st = prepare_rope(a, dev, hs, &rope)) != NEOX_OK) return st;
+
+  neox::FwdParams p;
+  fill_shape(a, rope, &p.a);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.sq = to_internal(s ? s[0] : def);
+  p.sk = to_internal(s ? s[1] : def);
+  p.sv = to_internal(s ? s[2] : def);
+  p.so = to_internal(s ? s[3] : def);
+  p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
+  if (neox::record_event(ev, 0, hs) != hipSuccess) return NEOX_E_LAUNCH;
+  const hipError_t e = a->dtype == NEOX_BF16 ? neox::launch_fwd_bf16(p, hs)
+                                             : neox::launch_fwd_f32(p, hs);
+  if (e != hipSuccess) return NEOX_E_LAUNCH;
+  return neox::record_event(ev, 1, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
+}
+
+int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_common(a);
+  if (st != NEOX_OK) return st;
+  const neox_strides def = contiguous(a);
+  const neox_strides* s = a->strides;
+  const int unit_in = a->dtype == NEOX_BF16 ? 8 : 4;
+  const int unit_out = (a->dtype == NEOX_BF16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
+  const void* ins[5] = {q, k, v, o, dout};
+  for (int t = 0; t < 5; ++t)
+    if ((st = check_tensor(ins[t], s ? s[t] : def, unit_in)) != NEOX_OK) return st;
+  void* outs[3] = {dq, dk, dv};
+  for (int t = 0; t < 3; ++t)
+    if ((st = check_tensor(outs[t], s ? s[5 + t] : def, unit_out)) != NEOX_OK) return st;
+  if (!lse) return NEOX_E_ARG;
+  if (!aligned16(lse)) return NEOX_E_ALIGN;
+  for (int t = 0; t < 3; ++t)
+    for (int u = 0; u < 5; ++u)
+      if (outs[t] == ins[u]) return NEOX_E_ARG;
+  const size_t need = neox_rope_attn_bwd_workspace_size(a->B, a->H, a->S, a->D);
+  if (!workspace || workspace_bytes < need) return NEOX_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NEOX_E_ALIGN;
+
+  int dev = 0;
+  if ((st = check_device(&dev)) != NEOX_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const float2* rope = nullptr;
+  if ((st = prepare_rope(a, dev, hs, &rope)) != NEOX_OK) return st;
+
+  neox::BwdParams p;
+  fill_shape(a, rope, &p.a);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const int64_t rows = (int64_t)a->B * a->H * a->S;
+  p.dq_acc = reinterpret_cast<float*>(workspace);
+  p.delta = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                     round256((size_t)rows * (size_t)a->D * 4u));
+  p.sq = to_internal(s ? s[0] : def);
+  p.sk = to_internal(s ? s[1] : def);
+  p.sv = to_internal(s ? s[2] : def);
+  p.so = to_internal(s ? s[3] : def);
+  p.sdo = to_internal(s ? s[4] : def);
+  p.sdq = to_internal(s ? s[5] : def);
+  p.sdk = to_internal(s ? s[6] : def);
+  p.sdv = to_internal(s ? s[7] : def);
+  p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
+  const hipError_t e = a->dtype == NEOX_BF16 ? neox::launch_bwd_bf16(p, hs, ev)
+                                             : neox::launch_bwd_f32(p, hs, ev);
+  return e == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
+}
+
+int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int S, int D, int rotary_dim, float rope_base, int causal,
+                       float softmax_scale, int dtype, void* stream) {
+  neox_attn_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.dtype = dtype;
+  a.pos = NEOX_POS_ROPE;
+  a.rotary_dim = rotary_dim;
+  a.rope_base = rope_base;
+  a.causal = causal;
+  a.softmax_scale = softmax_scale;
+  a.out_dtype = NEOX_OUT_SAME;
+  return neox_attn_fwd_ex(&a, q, k, v, o, lse, stream);
+}
+
+int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int S, int D, int rotary_dim, float rope_base, int causal,
+                       float softmax_scale, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  neox_attn_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.dtype = dtype;
+  a.pos = NEOX_POS_ROPE;
+  a.rotary_dim = rotary_dim;
+  a.rope_base = rope_base;
+  a.causal = causal;
+  a.softmax_scale = softmax_scale;
+  a.out_dtype = NEOX_OUT_SAME;
+  return neox_attn_bwd_ex(&a, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                          stream);
+}
+
+int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S) {
+  if (!host_offsets || B < 1 || n_docs < 1 || S < 1) return NEOX_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* row = host_offsets + (int64_t)b * (n_docs + 1);
+    if (row[0] != 0 || row[n_docs] != S) return NEOX_E_ARG;
+    for (int d = 0; d < n_docs; ++d)
+      if (row[d + 1] < row[d]) return NEOX_E_ARG;
+  }
+  return NEOX_OK;
+}
+
+int neox_rope_table_prepare(int max_S, int rotary_dim, float rope_base) {
+  if (max_S < 1 || rotary_dim < 0 || (rotary_dim & 1) || !finite_pos(rope_base))
+    return NEOX_E_ARG;
+  if (rotary_dim == 0) return NEOX_OK;
+  int dev = 0;
+  int st = check_device(&dev);
+  if (st != NEOX_OK) return st;
+  const float2* rope = nullptr;
+  return get_rope_table(dev, max_S, rotary_dim, rope_base, nullptr, &rope);
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+/*
+ * neoxattn.h -- C ABI of libneoxattn: exact causal multi-head attention with
+ * GPT-NeoX rotary position embedding (rotate-half, optionally partial), in a
+ * tiled IO-aware form, forward and backward, on AMD MI355X (gfx950).
+ *
+ * What is computed.  For every batch row b and head h, with positions
+ * t = 0..S-1 and R_t the rotary matrix below:
+ *     q~_i = R_i q_i,   k~_j = R_j k_j                        (v is not rotated)
+ *     s_ij = softmax_scale * (q~_i . k~_j) + bias_ij
+ *     lse_i = log sum_{j allowed} exp(s_ij)        (natural log, fp32)
+ *     o_i   = sum_{j allowed} exp(s_ij - lse_i) v_j
+ * allowed(i, j) = (causal == 0 or j <= i) and doc(i) == doc(j).
+ * The attention is exact: the GPT-NeoX pages state that FlashAttention-2 keeps
+ * the mathematical result and changes only tiling and memory traffic, with
+ * O(n) instead of O(n^2) memory ("GPT-NeoX 开源训练框架深度解读", section
+ * "问题二：注意力计算太慢").  No S x S matrix is ever stored.
+ *
+ * Rotary (NeoX style, on both Q and K: "FasterTransformer GPT-NeoX 推理指南",
+ * GptNeoX.h facts neox_rotary_style_ and section "模型配置", rotary_embedding
+ * 24 of size_per_head 96): with half = rotary_dim / 2 and, for p < half,
+ * theta_{t,p} = t * rope_base^(-2p / rotary_dim):
+ *     y_p        = x_p cos(theta) - x_{p+half} sin(theta)
+ *     y_{p+half} = x_{p+half} cos(theta) + x_p sin(theta)
+ *     y_d        = x_d                                  for d >= rotary_dim.
+ * ALiBi (the alternative position scheme, "GPT-NeoX 开源训练框架深度解读",
+ * section "架构创新"): bias_ij = -slope_h * (i - j), added after the scaling,
+ * default slope_h = 2^(-8 (h+1) / H).  With RoPE the bias is 0.
+ *
+ * Conventions for every entry point:
+ *  - Tensors q, k, v, o, dout, dq, dk, dv are [B, H, S, D] with the head dim
+ *    contiguous; by default fully contiguous, otherwise strided (see
+ *    neox_attn_args.strides).  lse is [B, H, S] contiguous fp32.
+ *  - Every pointer argument that names tensor data is a DEVICE pointer owned
+ *    by the caller; the library keeps no pointer past the call.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is enqueued on it and the call returns without waiting.
+ *  - Arguments are validated before any device work; a failed validation
+ *    returns a negative status and enqueues nothing.  Launch failures return
+ *    NEOX_E_LAUNCH.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Outputs are undefined after an error.
+ *  - Supported: D in {64, 96, 128}; 0 <= rotary_dim <= D, rotary_dim even;
+ *    rope_base > 0 and finite; softmax_scale > 0 and finite; B, H, S >= 1;
+ *    B*H*S < 2^31; tensor base pointers 16-byte aligned; row strides multiples
+ *    of 8 elements (bf16) or 4 elements (fp32).
+ *  - Rotary cos/sin table: the first call on a device for a (rotary_dim,
+ *    rope_base) pair, or for a longer S than that pair has seen, allocates a
+ *    table of S * rotary_dim * 4 bytes on the device and fills it (angles and
+ *    cos/sin in double, stored as fp32).  Tables live until the process ends.
+ *    neox_rope_table_prepare() builds one ahead of time, so that later calls
+ *    allocate nothing.
+ */
+#ifndef NEOXATTN_H
+#define NEOXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NEOX_OK 0
+#define NEOX_E_ARG (-1)         /* null pointer, bad size, bad scalar, bad enum */
+#define NEOX_E_UNSUPPORTED (-2) /* valid but not implemented (e.g. D = 80) */
+#define NEOX_E_ALIGN (-3)       /* base pointer or row stride misaligned */
+#define NEOX_E_WORKSPACE (-4)   /* workspace NULL or smaller than required */
+#define NEOX_E_LAUNCH (-5)      /* a kernel launch failed */
+#define NEOX_E_DEVICE (-6)      /* no usable gfx950 device / HIP runtime error */
+#define NEOX_E_ALLOC (-7)       /* rotary table allocation failed */
+
+/* Storage type of q, k, v, o, dout (and of dq, dk, dv unless out_dtype says fp32). */
+#define NEOX_F32 0
+#define NEOX_BF16 1
+
+/* Position scheme. */
+#define NEOX_POS_NONE 0
+#define NEOX_POS_ROPE 1
+#define NEOX_POS_ALIBI 2
+
+/* Output type selector of the _ex calls. */
+#define NEOX_OUT_SAME 0 /* outputs in the input storage type */
+#define NEOX_OUT_F32 1  /* outputs in fp32 */
+
+/* Element strides of one [B, H, S, D] tensor whose head dim is contiguous. */
+typedef struct neox_strides {
+  int64_t batch;
+  int64_t head;
+  int64_t seq;
+} neox_strides;
+
+/*
+ * Arguments of the _ex calls.
+ *  pos           NEOX_POS_NONE / NEOX_POS_ROPE / NEOX_POS_ALIBI.
+ *  rotary_dim,   used when pos == NEOX_POS_ROPE (rotary_dim may then be 0,
+ *  rope_base     which is plain attention); must be 0 otherwise.
+ *  alibi_slopes  device fp32 [H] or NULL for 2^(-8 (h+1) / H); pos == ALIBI only.
+ *  doc_offsets   device int32 [B][n_docs + 1] or NULL (one document per row).
+ *                Row b lists document starts: offsets[b][0] = 0, non-decreasing,
+ *                offsets[b][n_docs] = S; equal neighbours are empty documents.
+ *                Tokens of different documents never attend to each other.
+ *                Values are not read by the host; neox_check_doc_offsets()
+ *                validates a host copy.  Kernels clamp what they read, so
+ *                malformed offsets give undefined values but no stray access.
+ *  out_dtype     NEOX_OUT_SAME or NEOX_OUT_F32, for o (fwd) and dq, dk, dv (bwd).
+ *  strides       NULL for contiguous tensors, else 8 entries in the order
+ *                q, k, v, o, dout, dq, dk, dv (the fwd reads the first 4).
+ *  phase_events  NULL, or hipEvent_t handles (as void*) that the call records
+ *                on `stream` around its kernels, for timing by the caller: the
+ *                forward records [0] before and [1] after its kernel; the
+ *                backward records [0] before the preprocess kernel, [1] after
+ *                it, [2] after the main kernel(s) and [3] after the dq
+ *                finalize.  The events are owned by the caller.
+ */
+typedef struct neox_attn_args {
+  int B, H, S, D;
+  int dtype;
+  int pos;
+  int rotary_dim;
+  float rope_base;
+  const float* alibi_slopes;
+  int causal;
+  float softmax_scale;
+  const int32_t* doc_offsets;
+  int n_docs;
+  int out_dtype;
+  const neox_strides* strides;
+  void* const* phase_events;
+} neox_attn_args;
+
+/* Text of a status code (static storage, never NULL). */
+const char* neox_status_str(int status);
+
+/*
+ * Forward.  q, k, v: [B, H, S, D] of `dtype` (read only).  o: [B, H, S, D] of
+ * `dtype` (written).  lse: [B, H, S] fp32 natural-log logsumexp of each row's
+ * allowed scores (written; the backward needs it).  rotary_dim = 0 turns the
+ * rotation off.  Causal masking when causal != 0.
+ */
+int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int S, int D, int rotary_dim, float rope_base,
+                       int causal, float softmax_scale, int dtype, void* stream);
+
+/* Bytes of device workspace the backward needs: an fp32 [B, H, S, D] dq
+ * accumulator and an fp32 [B, H, S] row term, each 256-byte aligned.  Returns
+ * 0 for sizes that are invalid (<= 0) or overflow. */
+size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
+
+/*
+ * Backward.  Inputs q, k, v, o, dout ([B, H, S, D], `dtype`) and lse (from the
+ * forward with the same arguments) are read only.  dq, dk, dv ([B, H, S, D],
+ * `dtype`) are written and must not alias the inputs.  workspace: device
+ * memory of at least neox_rope_attn_bwd_workspace_size() bytes, 256-byte
+ * aligned, owned by the caller, overwritten by the call (its contents
+ * afterwards are unspecified).  dq is accumulated with fp32 atomics, so its
+ * last bits may differ from run to run; dk and dv are deterministic.
+ */
+int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int B, int H, int S, int D, int rotary_dim, float rope_base,
+                       int causal, float softmax_scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward with ALiBi, packed documents, strides and output type (see neox_attn_args). */
+int neox_attn_fwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* stream);
+
+/* Backward counterpart of neox_attn_fwd_ex; workspace as for neox_rope_attn_bwd. */
+int neox_attn_bwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side check of a HOST copy of doc_offsets ([B][n_docs + 1] int32):
+ * returns NEOX_OK when every row starts at 0, never decreases and ends at S,
+ * NEOX_E_ARG otherwise (or for a NULL pointer / bad sizes).  No device work.
+ */
+int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S);
+
+/*
+ * Builds (allocating if needed) the rotary cos/sin table of the current
+ * device for positions 0..max_S-1, rotary_dim and rope_base, and waits for it.
+ * Later calls with S <= max_S and the same pair allocate nothing.  Returns
+ * NEOX_OK, NEOX_E_ARG, NEOX_E_ALLOC or NEOX_E_DEVICE.
+ */
+int neox_rope_table_prepare(int max_S, int rotary_dim, float rope_base);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NEOXATTN_H */

@@ -1,0 +1,202 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments before touching any device.
+
+Only validation paths are called here (fake, never dereferenced pointers); no
+call that would launch a kernel runs without a GPU.
+"""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from causal_attention_neox_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_ARG, E_UNSUP, E_ALIGN, E_WS, E_LAUNCH, E_DEV, E_ALLOC = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+A1, A2, A3, A4, A5, A6, A7, A8, A9 = (P(0x10000 * n) for n in range(1, 10))  # 16-byte aligned
+
+
+@pytest.fixture(scope="session")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from causal_attention_neox_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(neox_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ("neox_rope_attn_fwd", "neox_rope_attn_bwd", "neox_rope_attn_bwd_workspace_size",
+              "neox_attn_fwd_ex", "neox_attn_bwd_ex", "neox_status_str"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover the header"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (neox_\w+)", out))
+    missing = set(declared_functions()) - exported
+    assert not missing, f"declared but not exported: {missing}"
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in (OK, E_ARG, E_UNSUP, E_ALIGN, E_WS, E_LAUNCH, E_DEV, E_ALLOC):
+        assert lib.neox_status_str(s)
+    assert lib.neox_status_str(OK) == b"ok"
+    assert lib.neox_status_str(12345) == b"unknown status"
+
+
+def fwd(lib, q=A1, k=A2, v=A3, o=A4, lse=A5, B=2, H=4, S=128, D=64, rd=16, base=1e4, causal=1,
+        scale=0.125, dtype=BF16):
+    return lib.neox_rope_attn_fwd(q, k, v, o, lse, B, H, S, D, rd, base, causal, scale, dtype,
+                                  None)
+
+
+def bwd(lib, ws=None, wsb=None, dq=A7, B=2, H=4, S=128, D=64, rd=16, dtype=BF16, **kw):
+    need = lib.neox_rope_attn_bwd_workspace_size(B, H, S, D)
+    ws = P(0x100000) if ws is None else ws
+    wsb = need if wsb is None else wsb
+    return lib.neox_rope_attn_bwd(kw.get("q", A1), A2, A3, A4, A5, A6, dq, A8, A9, B, H, S, D,
+                                  rd, 1e4, 1, 0.125, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_ARG), (dict(lse=None), E_ARG), (dict(B=0), E_ARG), (dict(H=-1), E_ARG),
+    (dict(S=0), E_ARG), (dict(D=0), E_ARG), (dict(D=80), E_UNSUP), (dict(D=256), E_UNSUP),
+    (dict(rd=15), E_ARG), (dict(rd=66), E_ARG), (dict(rd=-2), E_ARG),
+    (dict(base=0.0), E_ARG), (dict(base=float("inf")), E_ARG), (dict(base=float("nan")), E_ARG),
+    (dict(scale=0.0), E_ARG), (dict(scale=-1.0), E_ARG), (dict(scale=float("nan")), E_ARG),
+    (dict(dtype=7), E_ARG), (dict(q=P(0x10002)), E_ALIGN), (dict(o=P(0x10008)), E_ALIGN),
+    (dict(lse=P(0x10004)), E_ALIGN), (dict(B=1 << 16, H=1 << 8, S=1 << 8), E_ARG),
+])
+def test_forward_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None, wsb=0), E_WS), (dict(ws=P(0)), E_WS), (dict(ws=P(0x100010)), E_ALIGN),
+    (dict(dq=A1), E_ARG), (dict(dq=None), E_ARG), (dict(D=80), E_UNSUP), (dict(rd=3), E_ARG),
+])
+def test_backward_validation(lib, kw, status):
+    if kw.get("wsb") == 0:
+        assert bwd(lib, wsb=1) == E_WS
+        return
+    assert bwd(lib, **kw) == status
+
+
+def make_args(**kw):
+    a = _lib.NeoxAttnArgs()
+    a.B, a.H, a.S, a.D = 2, 4, 128, 64
+    a.dtype, a.pos, a.rotary_dim, a.rope_base = BF16, 1, 16, 1e4
+    a.causal, a.softmax_scale, a.out_dtype = 1, 0.125, 0
+    for n, v in kw.items():
+        setattr(a, n, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=9), E_ARG), (dict(pos=2), E_ARG),  # ALiBi with rotary_dim != 0
+    (dict(pos=0), E_ARG), (dict(out_dtype=3), E_ARG),
+    (dict(pos=2, rotary_dim=0, alibi_slopes=0x1002), E_ALIGN),
+    (dict(pos=1, alibi_slopes=0x1000), E_ARG),  # slopes without ALiBi
+    (dict(n_docs=3), E_ARG),                      # n_docs without offsets
+    (dict(doc_offsets=0x1000, n_docs=0), E_ARG),
+    (dict(doc_offsets=0x1002, n_docs=2), E_ALIGN),
+])
+def test_ex_validation(lib, kw, status):
+    a = make_args(**kw)
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == status
+
+
+def test_ex_strides_validation(lib):
+    strides = (_lib.NeoxStrides * 8)()
+    for n in range(8):
+        strides[n] = _lib.NeoxStrides(4 * 128 * 192, 128 * 192, 192)
+    a = make_args(strides=ctypes.cast(strides, ctypes.POINTER(_lib.NeoxStrides)))
+    # valid strides: validation passes, so the call stops at the device check on a CPU host
+    st = lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None)
+    assert st in (OK, E_DEV)
+    strides[1] = _lib.NeoxStrides(4 * 128 * 192, 128 * 192, 100)  # k rows not 16-byte aligned
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == E_ALIGN
+    strides[1] = _lib.NeoxStrides(-1, 0, 64)
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == E_ARG
+
+
+def test_null_args_struct(lib):
+    assert lib.neox_attn_fwd_ex(None, A1, A2, A3, A4, A5, None) == E_ARG
+    assert lib.neox_attn_bwd_ex(None, A1, A2, A3, A4, A5, A6, A7, A8, A9, A1, 1 << 30,
+                                None) == E_ARG
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present on this host")
+def test_valid_call_without_gpu_fails_loudly(lib):
+    """On a host without a GPU a fully valid call must return NEOX_E_DEVICE
+    (never silently compute anything elsewhere)."""
+    assert fwd(lib) == E_DEV
+    assert bwd(lib) == E_DEV
+
+
+def test_workspace_size_is_linear_in_sequence_length(lib):
+    """O(n) memory: the backward workspace is B*H*S*(D+1)*4 bytes up to
+    256-byte rounding, with no S^2 term."""
+    for (B, H, D) in [(1, 1, 64), (4, 64, 96), (1, 32, 128)]:
+        for S in (1, 17, 2048, 16384, 1 << 20):
+            rows = B * H * S
+            expect = ((rows * D * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+            assert lib.neox_rope_attn_bwd_workspace_size(B, H, S, D) == expect
+    assert lib.neox_rope_attn_bwd_workspace_size(0, 1, 1, 64) == 0
+    assert lib.neox_rope_attn_bwd_workspace_size(1 << 16, 1 << 8, 1 << 8, 64) == 0
+
+
+def test_check_doc_offsets(lib):
+    def chk(rows, S):
+        arr = np.ascontiguousarray(rows, dtype=np.int32)
+        return lib.neox_check_doc_offsets(arr.ctypes.data_as(P), arr.shape[0], arr.shape[1] - 1, S)
+    assert chk([[0, 10, 10, 30]], 30) == OK
+    assert chk([[0, 30], [0, 30]], 30) == OK
+    assert chk([[1, 30]], 30) == E_ARG
+    assert chk([[0, 29]], 30) == E_ARG
+    assert chk([[0, 20, 10, 30]], 30) == E_ARG
+    assert lib.neox_check_doc_offsets(None, 1, 1, 30) == E_ARG
+
+
+def test_rope_table_prepare_validation(lib):
+    assert lib.neox_rope_table_prepare(0, 16, 1e4) == E_ARG
+    assert lib.neox_rope_table_prepare(128, 15, 1e4) == E_ARG
+    assert lib.neox_rope_table_prepare(128, 16, -1.0) == E_ARG
+    assert lib.neox_rope_table_prepare(128, 0, 1e4) == OK  # nothing to build
+
+
+def test_generated_doc_layout_is_valid(lib):
+    from causal_attention_neox_amd.workloads import WORKLOADS, generate
+    wl = WORKLOADS["alibi_docs_s4096_d128"].with_sizes(H=1, D=64)
+    inp = generate(wl, with_dout=False)
+    offs = inp.doc_offsets
+    arr = np.ascontiguousarray(offs)
+    assert lib.neox_check_doc_offsets(arr.ctypes.data_as(P), arr.shape[0], arr.shape[1] - 1,
+                                      wl.S) == OK
+    for row in offs:
+        lengths = np.diff(row)
+        lengths = lengths[lengths > 0]
+        assert lengths.sum() == wl.S
+        assert lengths.min() >= wl.doc_min and lengths.max() <= wl.doc_max

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Small shapes are compared on every element; they span several tiles and
+ragged tails and cover the edge cases (S = 1, odd S, partial and odd rotary
+widths, rotary off, non-causal, ALiBi, packed documents including length-1
+documents).  The full-size workloads run on the GPU exactly as the benchmark
+launches them and are compared on sampled heads, which the oracle computes
+exactly (heads are independent).
+"""
+
+import numpy as np
+import pytest
+
+from causal_attention_neox_amd.workloads import WORKLOADS, generate, doc_offsets_from_lengths
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_attention_neox_amd._lib as L
+    L.load()  # fails loudly when the library is missing
+    return torch
+
+
+SMALL = [
+    # B, H, S, D, rd, dtype, causal, alibi
+    (1, 2, 1, 64, 64, "bf16", True, False),
+    (1, 2, 2, 64, 16, "bf16", True, False),
+    (1, 2, 3, 96, 24, "bf16", True, False),
+    (2, 2, 31, 128, 128, "bf16", True, False),
+    (1, 3, 33, 64, 2, "bf16", True, False),
+    (1, 2, 63, 96, 24, "bf16", True, False),
+    (2, 2, 65, 128, 0, "bf16", True, False),
+    (1, 2, 127, 64, 16, "bf16", True, False),
+    (1, 2, 129, 96, 96, "bf16", True, False),
+    (2, 2, 300, 128, 128, "bf16", True, False),
+    (1, 2, 257, 128, 40, "bf16", True, False),
+    (1, 2, 200, 64, 6, "bf16", True, False),
+    (1, 2, 190, 128, 128, "bf16", False, False),
+    (1, 4, 300, 128, 0, "bf16", True, True),
+    (1, 2, 150, 96, 0, "bf16", False, True),
+    (1, 2, 1, 64, 64, "f32", True, False),
+    (1, 2, 77, 64, 64, "f32", True, False),
+    (2, 2, 130, 96, 24, "f32", True, False),
+    (1, 2, 200, 128, 128, "f32", True, False),
+    (1, 2, 100, 128, 10, "f32", False, True),
+]
+
+
+def _id(c):
+    return f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}rd{c[4]}-{c[5]}{'' if c[6] else '-noncausal'}{'-alibi' if c[7] else ''}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_small_shapes_every_element(case):
+    B, H, S, D, rd, dt, causal, alibi = case
+    if alibi:
+        rd = 0
+    wl = pu.small_workload(B, H, S, D, rd, dtype=dt, causal=causal, alibi=alibi, seed=S * 7 + D)
+    inp = generate(wl, with_dout=True)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    gpu = pu.run_library(inp, backward=True)
+    ref = pu.oracle_heads(inp, heads)
+    pu.compare(gpu, ref, heads, dt, label=_id(case))
+
+
+DOC_CASES = [
+    # S, D, docs (lengths per row), alibi, causal
+    (96, 64, [[1, 1, 30, 64], [96]], False, True),
+    (200, 128, [[70, 1, 129], [64, 64, 64, 8]], True, True),
+    (300, 96, [[100, 200], [1, 299]], False, True),
+    (160, 128, [[33, 127], [160]], True, False),
+]
+
+
+@pytest.mark.parametrize("case", DOC_CASES, ids=[f"docs{i}" for i in range(len(DOC_CASES))])
+def test_packed_documents_every_element(case):
+    S, D, rows, alibi, causal = case
+    B = len(rows)
+    wl = pu.small_workload(B, 2, S, D, 0 if alibi else D // 2, causal=causal, alibi=alibi,
+                           seed=S + D)
+    inp = generate(wl, with_dout=True)
+    inp.doc_offsets = doc_offsets_from_lengths(rows, S)
+    heads = [(b, h) for b in range(B) for h in range(2)]
+    gpu = pu.run_library(inp, backward=True)
+    ref = pu.oracle_heads(inp, heads)
+    pu.compare(gpu, ref, heads, "bf16", label=f"docs S={S} D={D} alibi={alibi} causal={causal}")
+
+
+def test_fp32_workload_full():
+    """The fp32 forward workload (B=1, H=2, S=128, D=64, full rotary), every element."""
+    inp = generate(WORKLOADS["fp32_s128_d64"])
+    heads = [(0, 0), (0, 1)]
+    gpu = pu.run_library(inp, backward=False)
+    ref = pu.oracle_heads(inp, heads, backward=False)
+    pu.compare(gpu, ref, heads, "f32", label="fp32_s128_d64")
+
+
+FULL = ["bf16_s2048_d64_rd16", "neox20b_s2048_h64_d96_rd24", "alibi_docs_s4096_d128",
+        "rope_s2048_d128", "long_s16384_d128"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_heads(name):
+    wl = WORKLOADS[name]
+    inp = generate(wl)
+    print(f"[parity] {name}: generated, running GPU", flush=True)
+    gpu = pu.run_library(inp, backward=True)
+    for key, t in gpu.items():
+        assert bool(t.isfinite().all()), f"{name}: non-finite {key}"
+    last = (wl.B - 1, wl.H - 1)
+    heads = [(0, 0), last] if wl.S <= 4096 else [last]
+    print(f"[parity] {name}: oracle on heads {heads}", flush=True)
+    ref = pu.oracle_heads(inp, heads)
+    pu.compare(gpu, ref, heads, wl.dtype, label=name)
+
+
+def test_forward_is_deterministic_and_writes_every_element(gpu):
+    torch = gpu
+    wl = pu.small_workload(2, 3, 333, 128, 128, seed=11)
+    inp = generate(wl, with_dout=False)
+    q, k, v = (pu.to_device(inp, n) for n in ("q", "k", "v"))
+    outs = []
+    for _ in range(3):
+        o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        import causal_attention_neox_amd as neox
+        neox.neox_rope_attn_fwd(q, k, v, o, lse, 128)
+        torch.cuda.synchronize()
+        assert bool(o.isfinite().all()) and bool(lse.isfinite().all())
+        outs.append((o.clone(), lse.clone()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(lse, outs[0][1])
+
+
+def test_backward_writes_every_element(gpu):
+    torch = gpu
+    import causal_attention_neox_amd as neox
+    wl = pu.small_workload(1, 2, 257, 96, 24, seed=12)
+    inp = generate(wl)
+    q, k, v, do = (pu.to_device(inp, n) for n in ("q", "k", "v", "dout"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    neox.neox_rope_attn_fwd(q, k, v, o, lse, 24)
+    ws = torch.full((neox.neox_rope_attn_bwd_workspace_size(1, 2, 257, 96),), 255,
+                    dtype=torch.uint8, device="cuda")  # NaN-patterned workspace
+    grads = [torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda") for _ in range(3)]
+    neox.neox_rope_attn_bwd(q, k, v, o, do, lse, *grads, 24, workspace=ws)
+    torch.cuda.synchronize()
+    for g in grads:
+        assert bool(g.isfinite().all())
+
+
+def test_strided_packed_qkv_matches_contiguous(gpu):
+    """q, k, v as views of one [B, S, 3, H, D] buffer (the fused-QKV layout)."""
+    torch = gpu
+    import causal_attention_neox_amd as neox
+    wl = pu.small_workload(2, 4, 190, 64, 16, seed=13)
+    inp = generate(wl)
+    q, k, v, do = (pu.to_device(inp, n) for n in ("q", "k", "v", "dout"))
+    B, H, S, D = q.shape
+    packed = torch.stack([q, k, v], dim=0).permute(1, 3, 0, 2, 4).contiguous()  # [B,S,3,H,D]
+    qs, ks, vs = (packed[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert qs.stride(3) == 1 and not qs.is_contiguous()
+    ref = pu.run_library(inp, backward=True)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=16)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                     device="cuda")
+    neox.neox_attn_bwd_ex(qs, ks, vs, o, do, lse, *grads, rotary_dim=16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref["o"].view(torch.int16))
+    assert torch.equal(lse, ref["lse"])
+    assert torch.equal(grads[1].view(torch.int16), ref["dk"].view(torch.int16))
+    assert torch.equal(grads[2].view(torch.int16), ref["dv"].view(torch.int16))
+    assert (grads[0].float() - ref["dq"].float()).abs().max().item() < 1e-2  # fp32 atomics order
+
+
+def test_fp32_outputs_option(gpu):
+    wl = pu.small_workload(1, 2, 300, 128, 128, seed=14)
+    inp = generate(wl)
+    heads = [(0, 0), (0, 1)]
+    gpu_out = pu.run_library(inp, backward=True, out_f32=True)
+    for t in gpu_out.values():
+        assert t.dtype == gpu.float32
+    ref = pu.oracle_heads(inp, heads)
+    pu.compare(gpu_out, ref, heads, "bf16", label="out_f32")
+
+
+def test_autograd_wrapper(gpu):
+    torch = gpu
+    import causal_attention_neox_amd as neox
+    wl = pu.small_workload(1, 2, 100, 64, 16, seed=15)
+    inp = generate(wl)
+    q, k, v, do = (pu.to_device(inp, n) for n in ("q", "k", "v", "dout"))
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    o = neox.attention(q, k, v, rotary_dim=16)
+    o.backward(do)
+    ref = pu.run_library(inp, backward=True)
+    assert torch.equal(o.detach().view(torch.int16), ref["o"].view(torch.int16))
+    assert torch.equal(v.grad.view(torch.int16), ref["dv"].view(torch.int16))
+    assert torch.equal(k.grad.view(torch.int16), ref["dk"].view(torch.int16))
