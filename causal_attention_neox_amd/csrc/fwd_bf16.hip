@@ -6,39 +6,232 @@
 // tiles of 64 keys through LDS, keeps a running row max and row sum (online
 // softmax) in registers, and never materialises the S x S score matrix.  The
 // NeoX rotary rotation of Q and K ("FasterTransformer GPT-NeoX 推理指南",
-// neox_rotary_style_ / rotary_embedding) is applied while the rows are loaded.
+// neox_rotary_style_ / rotary_embedding) is applied while rows are loaded.
 //
-// Layout choices (one wave = 64 lanes = 32 queries):
-//  * Scores are computed transposed, S^T = K~ Q~^T, with v_mfma_f32_32x32x16_bf16:
-//    A = K~ rows from LDS, B = Q~ held in registers for the whole loop.  The
-//    accumulator gives lane l the scores of query l%32 against 16 keys per
-//    32-key block, so the row max / row sum need only one cross-lane step
-//    (lanes l and l^32) instead of a 32-lane reduction.
-//  * O is accumulated transposed, O^T += V^T P^T: A = V^T from LDS (V is stored
-//    transposed, with keys reordered inside groups of 16 so that the score
-//    accumulator registers are directly the B operand), B = P in registers.
-//    Each lane then owns one query row of O, so the online-softmax rescale is
-//    a per-lane multiply.
-//  * Workgroups are issued heaviest q-tile first; consecutive workgroup ids
-//    walk over heads, so with B*H a multiple of 8 every q-tile of a head lands
-//    on the same XCD (ids are dealt to the 8 XCDs round-robin) and shares its
-//    K/V through that XCD's L2.
+// Layout (one wave = 64 lanes = 32 queries):
+//  * S^T = K~ Q~^T on v_mfma_f32_32x32x16_bf16: A = K~ rows from LDS, B = Q~
+//    held in registers for the whole loop.  Lane l gets the scores of query
+//    l%32 against 16 keys per 32-key block, so the row max needs one lane swap
+//    (l <-> l^32) and the row sum is a per-lane partial until the end.
+//  * O^T += V^T P^T: B = P straight from the score registers; A = V^T read from
+//    the row-major V tile with ds_read_b64_tr_b16 (two 4-key reads per 8-key
+//    operand), so V needs no transposition anywhere.
+//  * Software pipeline: the next tile's K/V rows are fetched into registers
+//    while the current tile is computed from LDS, then rotated/stored into the
+//    other LDS buffer; one barrier per tile.
+//  * Tiles that need no mask (fully inside every row's allowed range) run a
+//    mask-free softmax; the running max is raised lazily (only when a row's
+//    max grows by more than 2^8 in the exp2 domain), so O and the row sum are
+//    rescaled rarely.
+//  * Workgroups are issued heaviest q-tile first, heads fastest: with B*H a
+//    multiple of 8 all q-tiles of a head share one XCD and its L2.
 #include "device_common.hpp"
 
 namespace neox {
 namespace {
 
-constexpr int BM = 128;      // query rows per workgroup (4 waves x 32)
-constexpr int BN = 64;       // keys per tile
-constexpr int NT = 256;      // threads per workgroup
-constexpr int PAD = 8;       // bf16 padding per LDS row
+constexpr int BM = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int BN = 64;   // keys per tile
+constexpr int NT = 256;  // threads per workgroup
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
+                                   (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
+}
+
+// LDS layout of a K or V tile: BN rows x D/8 chunks of 16 bytes, unpadded, chunk
+// c of row r at position r*(D/8) + (c ^ swizzle(r)).  The swizzles make the
+// MFMA operand reads conflict-free across the 64 LDS banks: K is read one row
+// per lane (16 B, rows 0..15 of a lane group must hit 16 different bank
+// groups); V is read with ds_read_b64_tr_b16 (4 rows x 4 chunks per 32 lanes).
+template <int D>
+struct Swz {
+  static __device__ __forceinline__ int k(int row) {
+    return D == 128 ? (row & 15) : (D == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3));
+  }
+  static __device__ __forceinline__ int v(int row) {
+    return D == 128 ? 4 * (row & 3) : (D == 64 ? 4 * ((row >> 1) & 1) : 0);
+  }
+};
+
+// Per-thread plan for staging one K/V tile.  V, and the K chunks outside the
+// rotary dims, go global -> LDS directly (global_load_lds_dwordx4: lane l of a
+// wave writes position 64*block + l, so each lane fetches the global chunk
+// that belongs at that position).  The rotary K dims go through registers as
+// "pair items" (row, W consecutive pairs: dims p0.. and half+p0..) and are
+// rotated before being written to LDS; for rotary widths that are not a
+// multiple of 8 every K chunk goes through registers (rotated element-wise).
 template <int D, int ROT>
+struct TilePlan {
+  static constexpr int CPR = D / 8;             // chunks per row
+  static constexpr int NB = CPR / 4;            // direct-load blocks per wave (of K and of V)
+  static constexpr bool PAIRS = ROT == 1 || ROT == 2;
+  static constexpr int W = ROT == 1 ? 8 : 4;    // pairs per pair item
+  static constexpr int NPAIR = PAIRS ? (BN * D / (2 * W) + NT - 1) / NT : 1;
+  static constexpr int NREG = ROT == 3 ? BN * CPR / NT : 1;
+  int kpos[NB];   // row << 8 | chunk of this lane's K position in block i (chunk -1: not direct)
+  int vpos[NB];
+  int pitem[NPAIR];            // row << 8 | p0, -1 unused
+  int plds[NPAIR];             // LDS element offset of dims p0.. (low 16) and half+p0.. (high 16)
+  u32x4 plo[NPAIR], phi[NPAIR];
+  int ritem[NREG];             // ROT 3: row << 8 | chunk
+  u32x4 rk[NREG];
+
+  __device__ __forceinline__ static int kp(int row, int chunk) {
+    return row * CPR + (chunk ^ Swz<D>::k(row));
+  }
+
+  __device__ __forceinline__ void init(int wave, int lane, int tid, int rd) {
+    const int rchunks = PAIRS ? rd / 8 : (ROT == 3 ? CPR : 0);  // K chunks not loaded directly
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int P = 64 * (wave + 4 * i) + lane;
+      const int row = P / CPR;
+      const int ck = (P % CPR) ^ Swz<D>::k(row);
+      const int cv = (P % CPR) ^ Swz<D>::v(row);
+      kpos[i] = ck < rchunks ? -1 : (row << 8) | ck;
+      vpos[i] = (row << 8) | cv;
+    }
+    const int half = rd >> 1;
+    const int slots = PAIRS ? half / W : 0;
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      const int it = tid + NT * i;
+      if (PAIRS && it < BN * slots) {
+        const int row = it / slots, p0 = (it % slots) * W;
+        pitem[i] = (row << 8) | p0;
+        const int lo = kp(row, p0 >> 3) * 8 + (p0 & 7);
+        const int hi = kp(row, (half + p0) >> 3) * 8 + ((half + p0) & 7);
+        plds[i] = lo | (hi << 16);
+      } else {
+        pitem[i] = -1;
+        plds[i] = 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const int it = tid + NT * i;
+      ritem[i] = ROT == 3 ? ((it / CPR) << 8) | (it % CPR) : -1;
+    }
+  }
+
+  // Issues the direct loads of tile rows [k0, k0 + BN) into Kt / Vt (rows past
+  // S repeat row S-1; those keys are masked) and fetches the register items.
+  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, int64_t ks,
+                                        const uint16_t* __restrict__ vb, int64_t vs, int k0,
+                                        int S, int rd, uint16_t* Kt, uint16_t* Vt, int wave) {
+    const bool full = k0 + BN <= S;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = wave + 4 * i;
+      {
+        const int row = vpos[i] >> 8, c = vpos[i] & 255;
+        const int r = full ? k0 + row : min(k0 + row, S - 1);
+        load_lds16(vb + (int64_t)r * vs + 8 * c, Vt + 512 * blk);
+      }
+      if (kpos[i] >= 0) {
+        const int row = kpos[i] >> 8, c = kpos[i] & 255;
+        const int r = full ? k0 + row : min(k0 + row, S - 1);
+        load_lds16(kb + (int64_t)r * ks + 8 * c, Kt + 512 * blk);
+      }
+    }
+    const int half = rd >> 1;
+    if (PAIRS) {
+#pragma unroll
+      for (int i = 0; i < NPAIR; ++i) {
+        if (pitem[i] >= 0) {
+          const int row = pitem[i] >> 8, p0 = pitem[i] & 255;
+          const int r = full ? k0 + row : min(k0 + row, S - 1);
+          const uint16_t* src = kb + (int64_t)r * ks + p0;
+          if (W == 8) {
+            plo[i] = *reinterpret_cast<const u32x4*>(src);
+            phi[i] = *reinterpret_cast<const u32x4*>(src + half);
+          } else {
+            const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+            const u32x2 b = *reinterpret_cast<const u32x2*>(src + half);
+            plo[i] = u32x4{a[0], a[1], 0u, 0u};
+            phi[i] = u32x4{b[0], b[1], 0u, 0u};
+          }
+        }
+      }
+    }
+    if (ROT == 3) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int row = ritem[i] >> 8, c = ritem[i] & 255;
+        const int r = min(k0 + row, S - 1);
+        rk[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)r * ks + 8 * c);
+      }
+    }
+  }
+
+  // Rotates the register items (angle of each row's position) into Kt.
+  __device__ __forceinline__ void store(uint16_t* Kt, const uint16_t* __restrict__ kb, int64_t ks,
+                                        int k0, int S, int rd, const float2* __restrict__ rope) {
+    const int half = rd >> 1;
+    if (PAIRS) {
+#pragma unroll
+      for (int i = 0; i < NPAIR; ++i) {
+        if (pitem[i] >= 0) {
+          const int row = pitem[i] >> 8, p0 = pitem[i] & 255;
+          const int pos = min(k0 + row, S - 1);
+          const f32x4* cs = reinterpret_cast<const f32x4*>(rope + (int64_t)pos * half + p0);
+          uint32_t lo[W / 2], hi[W / 2];
+#pragma unroll
+          for (int e2 = 0; e2 < W / 2; ++e2) {
+            const f32x4 c = cs[e2];  // (cos, sin) of pairs p0 + 2 e2 and p0 + 2 e2 + 1
+            const uint32_t a = plo[i][e2], bw = phi[i][e2];
+            const float x1a = bf_lo(a), x1b = bf_hi(a), x2a = bf_lo(bw), x2b = bf_hi(bw);
+            lo[e2] = pack2(x1a * c[0] - x2a * c[1], x1b * c[2] - x2b * c[3]);
+            hi[e2] = pack2(x2a * c[0] + x1a * c[1], x2b * c[2] + x1b * c[3]);
+          }
+          uint16_t* dlo = Kt + (plds[i] & 0xffff);
+          uint16_t* dhi = Kt + (plds[i] >> 16);
+          if (W == 8) {
+            *reinterpret_cast<u32x4*>(dlo) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *reinterpret_cast<u32x4*>(dhi) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            *reinterpret_cast<u32x2*>(dlo) = u32x2{lo[0], lo[1]};
+            *reinterpret_cast<u32x2*>(dhi) = u32x2{hi[0], hi[1]};
+          }
+        }
+      }
+    }
+    if (ROT == 3) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int row = ritem[i] >> 8, c = ritem[i] & 255;
+        const int r = min(k0 + row, S - 1);
+        u32x4 w = rk[i];
+        if (8 * c < rd) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf_lo(w[e]);
+            x[2 * e + 1] = bf_hi(w[e]);
+          }
+          rotate8_scalar(kb + (int64_t)r * ks, 8 * c, x, r, rd, rope);
+          w = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+        }
+        *reinterpret_cast<u32x4*>(Kt + 8 * kp(row, c)) = w;
+      }
+    }
+  }
+};
+
+template <int D, int ROT, bool ALIBI>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int KS = D + PAD;   // K~ tile row stride (elements)
-  constexpr int VS = BN + PAD;  // V^T tile row stride
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
 
   const AttnShape& a = p.a;
   const int S = a.S;
@@ -80,6 +273,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   if (a.causal && qlast < bhi) bhi = qlast;
   const int kt_lo = blo / BN, kt_hi = bhi / BN + 1;
 
+  // Prologue: fetch the first tile while Q~ is being loaded.
+  TilePlan<D, ROT> tp;
+  tp.init(wave, lane, tid, a.rd);
+  tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + 2 * TILE, wave);
+
   // Q~ of this lane's row as the B operand: chunk c holds dims 16c + 8hh .. +7.
   bf16x8 qreg[D / 16];
   {
@@ -88,104 +286,141 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int c = 0; c < D / 16; ++c) {
       const int d0 = 16 * c + 8 * hh;
       float x[8];
-      if (qi < S) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf_lo(w[e]);
-          x[2 * e + 1] = bf_hi(w[e]);
-        }
-        if (ROT != 0) rotate8_scalar(qrow, d0, x, qi, a.rd, a.rope);
-      } else {
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf_lo(w[e]);
+        x[2 * e + 1] = bf_hi(w[e]);
+      }
+      if (ROT != 0) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
+      if (qi >= S) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.0f;
       }
       qreg[c] = pack8(x);
     }
   }
+  tp.store(lds, kb, p.sk.s, kt_lo * BN, S, a.rd, a.rope);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  const float sl2 = a.alibi ? alibi_slope_log2(a, h) : 0.0f;
+  const float sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
   const float c2 = a.scale_log2;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY;  // running max in the exp2 domain (raised lazily)
+  float l_run = 0.0f;       // this lane's partial row sum (its 16 keys per block)
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
+  // Per-lane LDS operand addressing.  K~ A operand: row ql (+32 per block),
+  // chunk 2c + hh.  V^T via transposed reads: lane 16g + j reads 4 dims
+  // (chunk 4 db + 2 (g&1) + (j&3)/2, half (j&1)) of key 16 cp + 4 hh + j/4 (+8).
+  const int krow0 = ql * CPR, krow1 = (32 + ql) * CPR;
+  const int ksw0 = Swz<D>::k(ql), ksw1 = Swz<D>::k(32 + ql);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int vkey = 4 * hh + (j16 >> 2);
+  const int vsw = Swz<D>::v(vkey);  // same for keys vkey + 16 cp and vkey + 8
+  const int vch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int vhalf = 4 * (j16 & 1);
+
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int k0 = kt * BN;
-    __syncthreads();
-    load_tile<D, ROT, BN, NT, true, false, false>(kb, p.sk.s, k0, S, a.rd, a.rope, Ks, KS,
-                                                  nullptr, 0, tid);
-    load_tile<D, 0, BN, NT, false, true, true>(vb, p.sv.s, k0, S, 0, nullptr, nullptr, 0, Vt,
-                                               VS, tid);
-    __syncthreads();
+    const int buf = (kt - kt_lo) & 1;
+    const uint16_t* Kc = lds + buf * TILE;
+    const uint16_t* Vc = lds + (2 + buf) * TILE;
+    const bool more = kt + 1 < kt_hi;
+    if (more)
+      tp.fetch(kb, p.sk.s, vb, p.sv.s, k0 + BN, S, a.rd, lds + (buf ^ 1) * TILE,
+               lds + (2 + (buf ^ 1)) * TILE, wave);
 
     const bool lane_any = (k0 <= hi) && (k0 + BN - 1 >= lo);
-    if (!__any(lane_any)) continue;
-    const bool lane_full = (k0 >= lo) && (k0 + BN - 1 <= hi);
-    const bool need_mask = !__all(lane_full);
+    if (__any(lane_any)) {
+      const bool lane_full = (k0 >= lo) && (k0 + BN - 1 <= hi);
+      const bool need_mask = !__all(lane_full);
 
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 ka0 = lds_read8(Ks + ql * KS + 16 * c + 8 * hh);
-      const bf16x8 ka1 = lds_read8(Ks + (32 + ql) * KS + 16 * c + 8 * hh);
-      sacc[0] = mfma32x32x16(ka0, qreg[c], sacc[0]);
-      sacc[1] = mfma32x32x16(ka1, qreg[c], sacc[1]);
-    }
-
-    // Scores in the log2 domain; key of register r of block blk:
-    // k0 + 32 blk + 8 (r/4) + 4 hh + r%4.
-    float t[32];
-    const float abase = sl2 * (float)(k0 + 4 * hh - qi);
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 ka0 = lds_read8(Kc + 8 * (krow0 + ((2 * c + hh) ^ ksw0)));
+        const bf16x8 ka1 = lds_read8(Kc + 8 * (krow1 + ((2 * c + hh) ^ ksw1)));
+        sacc[0] = mfma32x32x16(ka0, qreg[c], sacc[0]);
+        sacc[1] = mfma32x32x16(ka1, qreg[c], sacc[1]);
+      }
+      // Register r of block blk: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.  The
+      // scores stay in the accumulator registers: raw (RoPE) or exp2-domain
+      // with the ALiBi bias (ALiBi).
+      if (ALIBI) {
+        const float base = sl2 * (float)(k0 + 4 * hh - qi);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int koff = 32 * blk + 8 * (r >> 2) + (r & 3);
-        float x = sacc[blk][r] * c2;
-        if (a.alibi) x += abase + sl2 * (float)koff;
-        if (need_mask) {
-          const int j = k0 + 4 * hh + koff;
-          if (j < lo || j > hi) x = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            sacc[blk][r] = __builtin_fmaf(sacc[blk][r], c2,
+                                          base + sl2 * (float)(32 * blk + 8 * (r >> 2) + (r & 3)));
+      }
+      if (need_mask) {
+        const int jlo = lo - k0 - 4 * hh, jhi = hi - k0 - 4 * hh;  // allowed key offsets
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = 32 * blk + 8 * (r >> 2) + (r & 3);
+            if (ko < jlo || ko > jhi) sacc[blk][r] = -INFINITY;
+          }
+      }
+      float mx = fmaxf(sacc[0][0], fmaxf(sacc[0][1], sacc[0][2]));
+#pragma unroll
+      for (int i = 3; i < 31; i += 2)
+        mx = fmaxf(mx, fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
+      mx = fmaxf(mx, sacc[1][15]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mt = ALIBI ? mx : mx * c2;  // tile max in the exp2 domain
+      if (__any(mt > m_ref + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[blk][r];
+          sacc[blk][r] = ALIBI ? fast_exp2(x - m_use) : fast_exp2(__builtin_fmaf(x, c2, -m_use));
+          l_run += sacc[blk][r];
         }
-        t[16 * blk + r] = x;
-      }
-    }
-    float mloc = t[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mloc = fmaxf(mloc, t[i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      t[i] = fast_exp2(t[i] - m_use);
-      psum += t[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
 
 #pragma unroll
-    for (int cp = 0; cp < BN / 16; ++cp) {
-      const bf16x8 pb = pack8(t + 16 * (cp >> 1) + 8 * (cp & 1));
+      for (int cp = 0; cp < BN / 16; ++cp) {
+        float pv[8];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 va = lds_read8(Vt + (32 * db + ql) * VS + 16 * cp + 8 * hh);
-        oacc[db] = mfma32x32x16(va, pb, oacc[db]);
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[cp >> 1][8 * (cp & 1) + e];
+        const bf16x8 pb = pack8(pv);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int vc = (4 * db + vch) ^ vsw;
+          const uint16_t* vp = Vc + 8 * ((16 * cp + vkey) * CPR + vc) + vhalf;
+          const s16x4 v0 = lds_read_tr4(vp);
+          const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = mfma32x32x16(va, pb, oacc[db]);
+        }
       }
     }
+    if (more) tp.store(lds + (buf ^ 1) * TILE, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // Epilogue: o = O / l, lse = (m + log2 l) ln 2.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qi < S) {
-    if (hh == 0) p.lse[(int64_t)bh * S + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (hh == 0) p.lse[(int64_t)bh * S + qi] = (m_ref + __log2f(l_tot)) * kLn2;
     // Register r of block db holds dim 32 db + 8 (r/4) + 4 hh + r%4.
     if (p.out_f32) {
       float* orow = (float*)p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s;
@@ -213,28 +448,36 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int ROT>
+template <int D, int ROT, bool ALIBI>
 hipError_t launch_d(const FwdParams& p, hipStream_t st) {
   const int nqt = (p.a.S + BM - 1) / BM;
   const dim3 grid((unsigned)(nqt * p.a.B * p.a.H));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROT>), grid, dim3(NT), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROT, ALIBI>), grid, dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool ALIBI>
 hipError_t launch_rot(const FwdParams& p, hipStream_t st) {
-  if (p.a.rd == 0) return launch_d<D, 0>(p, st);
-  if (p.a.rd % 8 == 0) return launch_d<D, 1>(p, st);
-  return launch_d<D, 2>(p, st);
+  const int rd = p.a.rd;
+  if (rd == 0) return launch_d<D, 0, ALIBI>(p, st);
+  if (rd % 16 == 0) return launch_d<D, 1, ALIBI>(p, st);
+  if (rd % 8 == 0) return launch_d<D, 2, ALIBI>(p, st);
+  return launch_d<D, 3, ALIBI>(p, st);
+}
+
+template <int D>
+hipError_t launch_alibi(const FwdParams& p, hipStream_t st) {
+  if (p.a.alibi) return launch_d<D, 0, true>(p, st);  // ALiBi runs without rotary
+  return launch_rot<D, false>(p, st);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st) {
   switch (p.a.D) {
-    case 64: return launch_rot<64>(p, st);
-    case 96: return launch_rot<96>(p, st);
-    case 128: return launch_rot<128>(p, st);
+    case 64: return launch_alibi<64>(p, st);
+    case 96: return launch_alibi<96>(p, st);
+    case 128: return launch_alibi<128>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
