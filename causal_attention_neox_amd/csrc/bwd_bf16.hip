@@ -2,67 +2,181 @@
 //
 // Recompute-based backward of the tiled exact attention (GPT-NeoX trains with
 // the FlashAttention-2 form, "GPT-NeoX 开源训练框架深度解读", section
-// "问题二：注意力计算太慢"): the probabilities are rebuilt from the forward's
-// row logsumexp instead of being stored, so memory stays O(S).
+// "问题二：注意力计算太慢"): probabilities are rebuilt from the forward's row
+// logsumexp instead of being stored, so memory stays O(S).
 //
-//   pre:      Delta_i = dO_i . o_i, and the fp32 dQ~ accumulator is zeroed.
+//   prep:     per row, Delta_i = dO_i . o_i, nlse_i = -lse_i log2(e) (with the
+//             ALiBi row term folded in), the fp32 dQ~ accumulator zeroed, and
+//             the rotated rows q~ = R q, k~ = R k written once to the workspace
+//             (NeoX rotate-half, "FasterTransformer GPT-NeoX 推理指南"), so the
+//             main loop never rotates.
 //   main:     one workgroup per (batch, head, 128 keys); K~ and V stay in
-//             registers/LDS while q-tiles of 64 rows stream through:
-//               S = Q~ K~^T,  P = exp(S*scale - lse),  dP = dO V^T,
-//               dS = P (dP - Delta) * scale,
-//               dV~^T += dO^T P,   dK~^T += Q~^T dS   (registers),
-//               dQ~ += dS K~                          (fp32 atomics).
+//             registers (and K~ in LDS) while q-tiles of 64 rows stream through:
+//               S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
+//               dS = P (dP - Delta) scale,
+//               dV^T += dO^T P,   dK~^T += Q~^T dS   (registers),
+//               dQ~ += dS K~                       (fp32 atomics, coalesced).
 //             The epilogue applies R^T (rotation by -theta) to dK~ and writes
 //             dK and dV.
 //   finalize: dq = R^T dQ~, cast to the output type.
 //
 // Orientation: S and dP use M = queries, N = keys, so each lane owns one key
-// (column) and the P / dS registers are directly the B operand of the dV^T and
-// dK^T products; Q~^T and dO^T are staged transposed with the query order
-// permuted inside groups of 16 to match that register order.  dS is written to
-// LDS once per tile for the dQ product, which needs the other orientation.
+// and P / dS are directly the B operands of the dV^T and dK~^T products.  The
+// transposed operands (dO^T, Q~^T, dS^T, K~^T) come from row-major LDS tiles
+// through ds_read_b64_tr_b16.  Q~ and dO tiles go global -> LDS directly
+// (global_load_lds_dwordx4), double buffered with dS, one barrier per tile.
 #include "device_common.hpp"
 
 namespace neox {
 namespace {
 
 constexpr int BNK = 128;  // keys per workgroup (4 waves x 32)
-constexpr int BMQ = 64;   // queries per streamed tile
 constexpr int NT = 256;
-constexpr int PAD = 8;
-
+// Queries per streamed tile: 64, or 32 at D = 128 where the stationary
+// operands and accumulators leave less room for the score tiles.
 template <int D>
-struct BwdSmem {
-  static constexpr int QS = D + PAD;    // row-major Q~ / dO stride
-  static constexpr int TS = BMQ + PAD;  // transposed Q~^T / dO^T stride
-  static constexpr int SS = BNK + PAD;  // dS [query][key] stride
-  static constexpr int KTS = BNK + PAD; // K~^T [dim][key] stride
-  static constexpr int OFF_QS = 0;
-  static constexpr int OFF_QT = OFF_QS + BMQ * QS;
-  static constexpr int OFF_DOS = OFF_QT + D * TS;
-  static constexpr int OFF_DOT = OFF_DOS + BMQ * QS;
-  static constexpr int OFF_DSS = OFF_DOT + D * TS;
-  static constexpr int OFF_KT = OFF_DSS + BMQ * SS;
-  static constexpr int OFF_F = OFF_KT + D * KTS;     // fp32 area (lse2, delta)
-  static constexpr int N16 = OFF_F + 2 * (2 * BMQ);  // in uint16 units
-  static constexpr int FS = D + 4;                   // epilogue staging stride (floats)
-  static_assert(OFF_F % 8 == 0, "fp32 area must be 16-byte aligned");
-  static_assert(BNK * QS <= OFF_DOS, "K~ staging must fit in the Q~ areas");
-  static_assert(BNK * FS * 2 <= N16, "epilogue staging must fit");
+struct QTile {
+  static constexpr int BMQ = D == 128 ? 32 : 64;
 };
 
-template <int D, int ROT>
-__global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
-  using L = BwdSmem<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::N16];
-  uint16_t* Qs = smem + L::OFF_QS;
-  uint16_t* Qt = smem + L::OFF_QT;
-  uint16_t* dOs = smem + L::OFF_DOS;
-  uint16_t* dOt = smem + L::OFF_DOT;
-  uint16_t* dSs = smem + L::OFF_DSS;
-  uint16_t* KtT = smem + L::OFF_KT;
-  float* lse2s = reinterpret_cast<float*>(smem + L::OFF_F);
-  float* dels = lse2s + BMQ;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ bf16x8 tr8(const uint16_t* p, int second) {
+  const s16x4 a = tr4(p), b = tr4(p + second);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
+                                   (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
+}
+
+// LDS tiles are rows of C 16-byte chunks, unpadded; chunk c of row r sits at
+// r*C + (c ^ swz(r)).  The swizzle keeps both access patterns conflict-free on
+// the 64 banks: 16 B row reads (16 rows x same chunk per lane group) and the
+// transposed ds_read_b64_tr_b16 reads (4 rows x 4 chunks per 32 lanes).
+template <int C>
+__device__ __forceinline__ int swz(int row) {
+  return C == 16 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                 : (C == 12 ? ((row >> 2) & 3)
+                            : (C == 8 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : 0));
+}
+template <int C>
+__device__ __forceinline__ int tpos(int row, int chunk) {
+  return row * C + (chunk ^ swz<C>(row));
+}
+
+// ------------------------------------------------------------------------ prep
+
+// One wave per row, 16 B per lane: lanes 0..D/8-1 of the wave hold chunks of
+// q, k, o, dO of the row.  The rotary partners (dims +- rd/2) are exchanged
+// through a per-wave LDS row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int C = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][2][D];
+  const AttnShape& a = p.a;
+  const int S = a.S;
+  const int64_t rows = (int64_t)a.B * a.H * S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;  // whole waves only
+  const int bh = (int)(r / S), i = (int)(r % S);
+  const int b = bh / a.H, h = bh % a.H;
+  const bool act = lane < C;
+  const int d0 = 8 * lane;
+  float sum = 0.0f;
+  if (act) {
+    const u32x4 ow = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b +
+                                                     h * p.so.h + (int64_t)i * p.so.s + d0);
+    const u32x4 gw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b +
+                                                     h * p.sdo.h + (int64_t)i * p.sdo.s + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum = fmaf(bf_lo(ow[e]), bf_lo(gw[e]), sum);
+      sum = fmaf(bf_hi(ow[e]), bf_hi(gw[e]), sum);
+    }
+    float* acc = p.dq_acc + r * D + d0;
+    *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if (lane == 0) {
+    p.delta[r] = sum;
+    float nl = -p.lse[r] * kLog2e;
+    if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)i;
+    p.nlse[r] = nl;
+  }
+  const int rd = a.rd;
+  if (rd == 0) return;
+  const int half = rd >> 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* src = t == 0 ? (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h + (int64_t)i * p.sq.s
+                                 : (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h + (int64_t)i * p.sk.s;
+    uint16_t* dst = (t == 0 ? p.qrot : p.krot) + r * D + d0;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (act) {
+      w = *reinterpret_cast<const u32x4*>(src + d0);
+      *reinterpret_cast<u32x4*>(&rowbuf[wave][t][d0]) = w;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (act) {
+      if (d0 < rd) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf_lo(w[e]);
+          x[2 * e + 1] = bf_hi(w[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = d0 + e;
+          if (d < rd) {
+            const bool first = d < half;
+            const int pp = first ? d : d - half;
+            const float xp = bf2f(rowbuf[wave][t][first ? d + half : d - half]);
+            const float2 cs = a.rope[(int64_t)i * half + pp];
+            x[e] = first ? (x[e] * cs.x - xp * cs.y) : (x[e] * cs.x + xp * cs.y);
+          }
+        }
+        w = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+      }
+      *reinterpret_cast<u32x4*>(dst) = w;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ main
+
+template <int D>
+struct BwdLds {
+  static constexpr int BMQ = QTile<D>::BMQ;
+  static constexpr int C = D / 8;
+  static constexpr int KT = 0;                   // K~ [BNK][D]
+  static constexpr int Q0 = KT + BNK * D;        // Q~ tiles [BMQ][D] x2
+  static constexpr int G0 = Q0 + 2 * BMQ * D;    // dO tiles x2
+  static constexpr int DS0 = G0 + 2 * BMQ * D;   // dS tiles [BNK][BMQ] x2 (rows of BMQ/8 chunks)
+  static constexpr int F0 = DS0 + 2 * BNK * BMQ; // floats: nlse x2, Delta x2 (BMQ each)
+  static constexpr int N16 = F0 + 2 * 4 * BMQ;   // total in uint16 units
+  static_assert((F0 * 2) % 16 == 0, "float area alignment");
+};
+
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
+  using L = BwdLds<D>;
+  constexpr int BMQ = L::BMQ;
+  constexpr int QB = BMQ / 32;   // 32-query blocks per tile
+  constexpr int CS = BMQ / 8;    // 16-byte chunks per dS row
+  constexpr int C = L::C;
+  constexpr int NB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[L::N16];
+  float* fl = reinterpret_cast<float*>(lds + L::F0);  // nlse[2][BMQ], delta[2][BMQ]
 
   const AttnShape& a = p.a;
   const int S = a.S;
@@ -72,16 +186,21 @@ __global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4, j16 = lane & 15;
   const int k0 = kt * BNK;
   const int j = k0 + 32 * wave + ql;  // this lane's key
-  const int jc = j < S ? j : S - 1;
 
-  const uint16_t* qb = (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* kb = (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
+  const bool rot = a.rd > 0;
+  const uint16_t* qb = rot ? p.qrot + (int64_t)bh * S * D
+                           : (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
+  const int64_t qs = rot ? D : p.sq.s;
+  const uint16_t* kb = rot ? p.krot + (int64_t)bh * S * D
+                           : (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
+  const int64_t ks = rot ? D : p.sk.s;
   const uint16_t* vb = (const uint16_t*)p.v + b * p.sv.b + h * p.sv.h;
-  const uint16_t* dob = (const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h;
-  const float* lseb = p.lse + (int64_t)bh * S;
-  const float* delb = p.delta + (int64_t)bh * S;
+  const uint16_t* gb = (const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h;
+  const float* nlb = p.nlse + (int64_t)bh * S;
+  const float* dlb = p.delta + (int64_t)bh * S;
   float* dqab = p.dq_acc + (int64_t)bh * S * D;
 
   // Queries that may see this lane's key: [qlo, qhi].
@@ -89,7 +208,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
   int qlo = a.causal ? j : 0, qhi = S - 1;
   if (drow) {
     int ds, de;
-    doc_bounds(drow, a.n_docs, S, jc, ds, de);
+    doc_bounds(drow, a.n_docs, S, j < S ? j : S - 1, ds, de);
     qhi = de - 1;
     if (!a.causal) qlo = ds;
   }
@@ -105,145 +224,279 @@ __global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
   }
   const int qt_lo = bqlo / BMQ, qt_hi = bqhi / BMQ + 1;
 
-  // Stationary K~ (rotated) and V.  K~ rows go through LDS once: row-major for
-  // the per-lane B operand, transposed for the dQ product.
-  load_tile<D, ROT, BNK, NT, true, true, false>(kb, p.sk.s, k0, S, a.rd, a.rope, Qs, L::QS, KtT,
-                                                L::KTS, tid);
-  __syncthreads();
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // Direct-load plans: tile position P = 64 * block + lane -> (row, chunk).
+  // K~: BNK*C/64 blocks over 4 waves; Q~ and dO tiles: BMQ*C/64 = C blocks.
+  constexpr int NKB = BNK * C / 64 / 4;
+  constexpr int NQB = BMQ * C / 64 / 4;
+  int qoff[NQB], goff[NQB];
+#pragma unroll
+  for (int n = 0; n < NQB; ++n) {
+    const int P = 64 * (wave + 4 * n) + lane;
+    const int row = P / C, ch = (P % C) ^ swz<C>(row);
+    qoff[n] = (int)(row * qs) + 8 * ch;
+    goff[n] = (int)(row * p.sdo.s) + 8 * ch;
+  }
+  auto fetch_q = [&](int qt, int buf) {
+    const int q0 = qt * BMQ;
+    uint16_t* Qt = lds + L::Q0 + buf * BMQ * D;
+    uint16_t* Gt = lds + L::G0 + buf * BMQ * D;
+    if (q0 + BMQ <= S) {
+      const uint16_t* q_t = qb + (int64_t)q0 * qs;
+      const uint16_t* g_t = gb + (int64_t)q0 * p.sdo.s;
+#pragma unroll
+      for (int n = 0; n < NQB; ++n) {
+        load_lds16(q_t + qoff[n], Qt + 512 * (wave + 4 * n));
+        load_lds16(g_t + goff[n], Gt + 512 * (wave + 4 * n));
+      }
+      if ((S & 3) == 0) {  // rows of nlse / Delta start 16-byte aligned
+        if (wave == 0 && lane < BMQ / 4)
+          load_lds16(nlb + q0 + 4 * lane, lds + L::F0 + buf * 2 * BMQ);
+        if (wave == 1 && lane < BMQ / 4)
+          load_lds16(dlb + q0 + 4 * lane, lds + L::F0 + 4 * BMQ + buf * 2 * BMQ);
+      } else if (wave < 2 && lane < BMQ / 4) {
+        const float* src = wave == 0 ? nlb : dlb;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = src[q0 + 4 * lane + e];
+        *reinterpret_cast<f32x4*>(fl + wave * 2 * BMQ + buf * BMQ + 4 * lane) = w;
+      }
+    } else {
+      // last tile: rows past S re-read row S-1 (their P is masked to 0)
+#pragma unroll
+      for (int n = 0; n < NQB; ++n) {
+        const int P = 64 * (wave + 4 * n) + lane;
+        const int row = P / C, ch = (P % C) ^ swz<C>(row);
+        const int rr = min(q0 + row, S - 1);
+        load_lds16(qb + (int64_t)rr * qs + 8 * ch, Qt + 512 * (wave + 4 * n));
+        load_lds16(gb + (int64_t)rr * p.sdo.s + 8 * ch, Gt + 512 * (wave + 4 * n));
+      }
+      // nlse / Delta: 4 floats per lane; rows past S get 0 and are masked
+      if (wave < 2 && lane < BMQ / 4) {
+        const float* src = wave == 0 ? nlb : dlb;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = q0 + 4 * lane + e;
+          w[e] = ii < S ? src[ii] : 0.0f;
+        }
+        *reinterpret_cast<f32x4*>(fl + wave * 2 * BMQ + buf * BMQ + 4 * lane) = w;
+      }
+    }
+  };
+
+  // Stationary K~ tile and the first q-tile.
+#pragma unroll
+  for (int n = 0; n < NKB; ++n) {
+    const int P = 64 * (wave + 4 * n) + lane;
+    const int row = P / C, ch = (P % C) ^ swz<C>(row);
+    const int rr = min(k0 + row, S - 1);
+    load_lds16(kb + (int64_t)rr * ks + 8 * ch, lds + L::KT + 512 * (wave + 4 * n));
+  }
+  fetch_q(qt_lo, 0);
+  bf16x8 vreg[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    kreg[c] = lds_read8(Qs + (32 * wave + ql) * L::QS + 16 * c + 8 * hh);
-    if (j < S) {
+    vreg[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    if (j < S)
       vreg[c] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(vb + (int64_t)j * p.sv.s + 16 * c + 8 * hh));
-    } else {
-      vreg[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  bf16x8 kreg[D / 16];
+  {
+    const int row = 32 * wave + ql;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kreg[c] = lds_read8(lds + L::KT + 8 * tpos<C>(row, 2 * c + hh));
+  }
 
-  const float sl2 = a.alibi ? alibi_slope_log2(a, h) : 0.0f;
+  // Per-lane LDS offsets (elements) of the row reads and transposed reads.
+  // Row reads (A of S and dP): row 32 qb + ql, chunk 2c + hh.
+  const int rsw = swz<C>(ql);  // rows ql and 32 + ql share the swizzle
+  // Transposed reads of a [rows][C chunks] tile: lane 16g + j16 supplies row
+  // 16 t + 4 hh + j16/4 (+8 for the second read), 4 columns at chunk
+  // 4 db + 2 (g&1) + (j16&3)/2, half (j16&1).
+  const int trow = 4 * hh + (j16 >> 2);
+  const int tch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int thalf = 4 * (j16 & 1);
+  int taddr[2][NB];  // [second read][dim block] element offsets within a [*][D] tile
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+      taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) + thalf;
+  // dS tiles: [BNK keys][BMQ queries] rows of CS chunks.  dQ A operand:
+  // supplier lane reads key row 16 kc + 8 hh + j16/4 (+4), queries at chunk
+  // 4 qb + 2 (g&1) + (j16&3)/2.
+  const int srow = 8 * hh + (j16 >> 2);
+  int saddr[2][QB];  // [second read (+4 keys)][qb]
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int qb2 = 0; qb2 < QB; ++qb2)
+      saddr[s2][qb2] =
+          8 * ((srow + 4 * s2) * CS + ((4 * qb2 + tch) ^ swz<CS>(srow + 4 * s2))) + thalf;
+  // dQ B operand (K~ transposed): key row 16 kc + 8 hh + j16/4 (+4), dims at
+  // chunk 4 db + 2 (g&1) + (j16&3)/2.
+  int kaddr[2];  // [second read] for this wave's dim block (db = wave)
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    kaddr[s2] = 8 * ((srow + 4 * s2) * C + ((4 * (wave < NB ? wave : 0) + tch) ^ swz<C>(srow + 4 * s2))) + thalf;
+  // dS write: this lane's key row (32 wave + ql), 4 queries 32 qb + 8 a4 + 4 hh.
+  const int wrow = 32 * wave + ql;
+  const int wsw = swz<CS>(wrow);
+
   const float c2 = a.scale_log2;
   const float scale = a.scale;
-  f32x16 dvacc[D / 32], dkacc[D / 32];
+  const float slj = ALIBI ? alibi_slope_log2(a, h) * (float)j : 0.0f;
+  f32x16 dvacc[NB], dkacc[NB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < NB; ++db) {
     dvacc[db] = f32x16{};
     dkacc[db] = f32x16{};
   }
 
   for (int qt = qt_lo; qt < qt_hi; ++qt) {
+    const int buf = (qt - qt_lo) & 1;
     const int q0 = qt * BMQ;
-    load_tile<D, ROT, BMQ, NT, true, true, true>(qb, p.sq.s, q0, S, a.rd, a.rope, Qs, L::QS, Qt,
-                                                 L::TS, tid);
-    load_tile<D, 0, BMQ, NT, true, true, true>(dob, p.sdo.s, q0, S, 0, nullptr, dOs, L::QS, dOt,
-                                               L::TS, tid);
-    if (tid < BMQ) {
-      const int i = q0 + tid;
-      lse2s[tid] = i < S ? lseb[i] * kLog2e : INFINITY;
-      dels[tid] = i < S ? delb[i] : 0.0f;
-    }
-    __syncthreads();
+    const uint16_t* Qt = lds + L::Q0 + buf * BMQ * D;
+    const uint16_t* Gt = lds + L::G0 + buf * BMQ * D;
+    uint16_t* DSt = lds + L::DS0 + buf * BNK * BMQ;
+    const float* nlt = fl + buf * BMQ;
+    const float* dlt = fl + 2 * BMQ + buf * BMQ;
+    if (qt + 1 < qt_hi) fetch_q(qt + 1, buf ^ 1);
 
-    const bool lane_any = (q0 + BMQ - 1 >= qlo) && (q0 <= qhi);
-    if (__any(lane_any)) {
+    // Every wave computes every tile (fully masked rows give P = dS = 0): a
+    // skip branch here would split the loop-carried accumulators across paths.
+    {
       const bool lane_full = (q0 >= qlo) && (q0 + BMQ - 1 <= qhi);
       const bool need_mask = !__all(lane_full);
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      f32x16 dpacc[2] = {f32x16{}, f32x16{}};
+      f32x16 sacc[QB], dpacc[QB];
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) {
+        sacc[qb2] = f32x16{};
+        dpacc[qb2] = f32x16{};
+      }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-          const bf16x8 qa = lds_read8(Qs + (32 * qb2 + ql) * L::QS + 16 * c + 8 * hh);
-          const bf16x8 da = lds_read8(dOs + (32 * qb2 + ql) * L::QS + 16 * c + 8 * hh);
-          sacc[qb2] = mfma32x32x16(qa, kreg[c], sacc[qb2]);
-          dpacc[qb2] = mfma32x32x16(da, vreg[c], dpacc[qb2]);
+        for (int qb2 = 0; qb2 < QB; ++qb2) {
+          const int off = 8 * ((32 * qb2 + ql) * C + ((2 * c + hh) ^ rsw));
+          sacc[qb2] = mfma32x32x16(lds_read8(Qt + off), kreg[c], sacc[qb2]);
+          dpacc[qb2] = mfma32x32x16(lds_read8(Gt + off), vreg[c], dpacc[qb2]);
         }
       }
-      // P and dS; register r of block qb2 is query q0 + 32 qb2 + 8 (r/4) + 4 hh + r%4.
-      float pv[32], dsv[32];
+      // P and dS in place; register r of block qb2 is query
+      // q0 + 32 qb2 + 8 (r/4) + 4 hh + r%4.
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
+      for (int qb2 = 0; qb2 < QB; ++qb2) {
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const int ioff = 32 * qb2 + 8 * a4 + 4 * hh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + ioff);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dels + ioff);
+          const f32x4 n4 = *reinterpret_cast<const f32x4*>(nlt + ioff);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + ioff);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a4 + e;
-            const int i = q0 + ioff + e;
-            float x = sacc[qb2][r] * c2 - l4[e];
-            if (a.alibi) x += sl2 * (float)(j - i);
-            float pr = fast_exp2(x);
-            if (need_mask && (i < qlo || i > qhi)) pr = 0.0f;
-            pv[16 * qb2 + r] = pr;
-            dsv[16 * qb2 + r] = pr * (dpacc[qb2][r] - d4[e]) * scale;
+            const float nl = ALIBI ? n4[e] + slj : n4[e];
+            float pr = fast_exp2(__builtin_fmaf(sacc[qb2][r], c2, nl));
+            if (need_mask) {
+              const int i = q0 + ioff + e;
+              if (i < qlo || i > qhi) pr = 0.0f;
+            }
+            sacc[qb2][r] = pr;
+            dpacc[qb2][r] = pr * (dpacc[qb2][r] - d4[e]) * scale;
           }
         }
       }
 #pragma unroll
       for (int qc = 0; qc < BMQ / 16; ++qc) {
-        const int base = 16 * (qc >> 1) + 8 * (qc & 1);
-        const bf16x8 pb = pack8(pv + base);
-        const bf16x8 sb = pack8(dsv + base);
+        float pv[8], sv[8];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 doa = lds_read8(dOt + (32 * db + ql) * L::TS + 16 * qc + 8 * hh);
-          const bf16x8 qta = lds_read8(Qt + (32 * db + ql) * L::TS + 16 * qc + 8 * hh);
-          dvacc[db] = mfma32x32x16(doa, pb, dvacc[db]);
-          dkacc[db] = mfma32x32x16(qta, sb, dkacc[db]);
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = sacc[qc >> 1][8 * (qc & 1) + e];
+          sv[e] = dpacc[qc >> 1][8 * (qc & 1) + e];
         }
-        // dS to LDS as [query][key] for the dQ product (same bf16 values).
+        const bf16x8 pb = pack8(pv);
+        const bf16x8 sb = pack8(sv);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const int off = taddr[0][db] + 16 * qc * D;
+          const bf16x8 ga = tr8(Gt + off, taddr[1][db] - taddr[0][db]);
+          const bf16x8 qa = tr8(Qt + off, taddr[1][db] - taddr[0][db]);
+          dvacc[db] = mfma32x32x16(ga, pb, dvacc[db]);
+          dkacc[db] = mfma32x32x16(qa, sb, dkacc[db]);
+        }
+        // dS (same bf16 values) to LDS, row = this lane's key, 4 queries each.
         const u32x4 w = __builtin_bit_cast(u32x4, sb);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int r = 8 * (qc & 1) + s;
-          const int row = 32 * (qc >> 1) + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const uint32_t word = w[s >> 1];
-          dSs[row * L::SS + 32 * wave + ql] = (uint16_t)((s & 1) ? (word >> 16) : (word & 0xffffu));
+        for (int hv = 0; hv < 2; ++hv) {
+          const int qoff2 = 16 * qc + 8 * hv + 4 * hh;  // first query of the 4
+          const int ch = qoff2 >> 3;
+          *reinterpret_cast<u32x2*>(DSt + 8 * (wrow * CS + (ch ^ wsw)) + (qoff2 & 7)) =
+              u32x2{w[2 * hv], w[2 * hv + 1]};
         }
+        // keep the operand reads of one query chunk together (bounds register use)
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 32; ++rr) dSs[(32 * hh + rr) * L::SS + 32 * wave + ql] = 0;
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // dQ~ += dS K~ for this tile: units of 32 queries x 32 dims over all 128 keys.
-    for (int u = wave; u < (D / 32) * (BMQ / 32); u += NT / 64) {
-      const int db = u % (D / 32), qb2 = u / (D / 32);
-      f32x16 acc = f32x16{};
+    // dQ~ += dS K~ for this tile: wave w < D/32 handles dims 32w..32w+31 for
+    // all the tile's queries (the 32-query blocks share the K~ operand).
+    if (wave < NB) {
+      f32x16 acc[QB];
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) acc[qb2] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < BNK / 16; ++kc) {
-        const bf16x8 sa = lds_read8(dSs + (32 * qb2 + ql) * L::SS + 16 * kc + 8 * hh);
-        const bf16x8 kt2 = lds_read8(KtT + (32 * db + ql) * L::KTS + 16 * kc + 8 * hh);
-        acc = mfma32x32x16(sa, kt2, acc);
-      }
+        const uint16_t* kt2 = lds + L::KT + kaddr[0] + 16 * kc * D;
+        const bf16x8 kb8 = tr8(kt2, kaddr[1] - kaddr[0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = q0 + 32 * qb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (i < S) unsafeAtomicAdd(dqab + (int64_t)i * D + 32 * db + ql, acc[r]);
+        for (int qb2 = 0; qb2 < QB; ++qb2) {
+          const uint16_t* sp = DSt + saddr[0][qb2] + 16 * kc * BMQ;
+          const bf16x8 sa = tr8(sp, saddr[1][qb2] - saddr[0][qb2]);
+          acc[qb2] = mfma32x32x16(sa, kb8, acc[qb2]);
+        }
+        if (kc & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      float* dst = dqab + (int64_t)(q0 + 4 * hh) * D + 32 * wave + ql;
+      if (q0 + BMQ <= S) {
+#pragma unroll
+        for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            unsafeAtomicAdd(dst + (32 * qb2 + 8 * (r >> 2) + (r & 3)) * D, acc[qb2][r]);
+      } else {
+#pragma unroll
+        for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int io = 32 * qb2 + 8 * (r >> 2) + (r & 3);
+            if (q0 + 4 * hh + io < S) unsafeAtomicAdd(dst + io * D, acc[qb2][r]);
+          }
       }
     }
-    __syncthreads();
   }
 
-  // Epilogue: stage dK~ and dV (fp32) by key row, then write rows coalesced.
-  float* stage = reinterpret_cast<float*>(smem);
+  // Epilogue: stage dK~ and dV (fp32) by key row over the (now idle) tile
+  // areas, then write rows coalesced; dK = R^T dK~.
+  __syncthreads();
+  float* stage = reinterpret_cast<float*>(lds + L::KT);
+  constexpr int FS = D + 4;
+  static_assert(BNK * FS * 2 <= L::F0, "epilogue staging must fit");
   const int half = a.rd >> 1;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pass == 0 ? dkacc[db][4 * a4 + e] : dvacc[db][4 * a4 + e];
-        *reinterpret_cast<f32x4*>(stage + (32 * wave + ql) * L::FS + 32 * db + 8 * a4 + 4 * hh) = w;
+        *reinterpret_cast<f32x4*>(stage + (32 * wave + ql) * FS + 32 * db + 8 * a4 + 4 * hh) = w;
       }
     __syncthreads();
     void* outp = pass == 0 ? p.dk : p.dv;
@@ -252,7 +505,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
       const int row = it / (D / 8), d0 = 8 * (it % (D / 8));
       const int jj = k0 + row;
       if (jj >= S) continue;
-      const float* srow = stage + row * L::FS;
+      const float* srow = stage + row * FS;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -280,72 +533,54 @@ __global__ __launch_bounds__(NT, 1) void bwd_bf16_kernel(BwdParams p) {
   }
 }
 
-// Delta_i = dO_i . o_i (fp32) and zeroing of the dQ~ accumulator; 16 lanes per row.
-template <int D, bool F32>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+// ------------------------------------------------------------------ finalize
+
+// dq = R^T dQ~ (rotation by -theta), cast to the output type.  One wave per
+// row, 8 dims per lane; rotary partners are exchanged through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32) {
+  __shared__ __attribute__((aligned(16))) float rowbuf[4][D];
   const int S = p.a.S;
   const int64_t rows = (int64_t)p.a.B * p.a.H * S;
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l16 = threadIdx.x & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
   if (r >= rows) return;
   const int bh = (int)(r / S), i = (int)(r % S);
   const int b = bh / p.a.H, h = bh % p.a.H;
-  float sum = 0.0f;
-  if (l16 < D / 8) {
-    const int d0 = 8 * l16;
-    if (F32) {
-      const float* orow = (const float*)p.o + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s + d0;
-      const float* grow = (const float*)p.dout + b * p.sdo.b + h * p.sdo.h + (int64_t)i * p.sdo.s + d0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum = fmaf(orow[e], grow[e], sum);
-    } else {
-      const uint16_t* orow = (const uint16_t*)p.o + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s + d0;
-      const uint16_t* grow =
-          (const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h + (int64_t)i * p.sdo.s + d0;
-      const u32x4 ow = *reinterpret_cast<const u32x4*>(orow);
-      const u32x4 gw = *reinterpret_cast<const u32x4*>(grow);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sum = fmaf(bf_lo(ow[e]), bf_lo(gw[e]), sum);
-        sum = fmaf(bf_hi(ow[e]), bf_hi(gw[e]), sum);
-      }
-    }
-    float* acc = p.dq_acc + r * D + d0;
-    *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  sum += __shfl_xor(sum, 8, 16);
-  sum += __shfl_xor(sum, 4, 16);
-  sum += __shfl_xor(sum, 2, 16);
-  sum += __shfl_xor(sum, 1, 16);
-  if (l16 == 0) p.delta[r] = sum;
-}
-
-// dq = R^T dQ~ (rotation by -theta), cast to the output type; 8 dims per thread.
-template <int D>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32) {
-  const int S = p.a.S;
-  const int64_t rows = (int64_t)p.a.B * p.a.H * S;
-  const int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (it >= rows * (D / 8)) return;
-  const int64_t r = it / (D / 8);
-  const int d0 = 8 * (int)(it % (D / 8));
-  const int bh = (int)(r / S), i = (int)(r % S);
-  const int b = bh / p.a.H, h = bh % p.a.H;
-  const float* acc = p.dq_acc + r * D;
+  const bool act = lane < D / 8;
+  const int d0 = 8 * lane;
   const int rd = p.a.rd, half = rd >> 1;
   float x[8];
+  if (act) {
+    const float* acc = p.dq_acc + r * D + d0;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(acc);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(acc + 4);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = d0 + e;
-    float y = acc[d];
-    if (d < rd) {
-      const bool first = d < half;
-      const float2 cs = p.a.rope[(int64_t)i * half + (first ? d : d - half)];
-      const float xp = acc[first ? d + half : d - half];
-      y = first ? (y * cs.x + xp * cs.y) : (y * cs.x - xp * cs.y);
+    for (int e = 0; e < 4; ++e) {
+      x[e] = lo[e];
+      x[4 + e] = hi[e];
     }
-    x[e] = y;
+    if (rd > 0) {
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][d0]) = lo;
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][d0 + 4]) = hi;
+    }
+  }
+  if (rd > 0) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  if (!act) return;
+  if (d0 < rd) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      if (d < rd) {
+        const bool first = d < half;
+        const float2 cs = p.a.rope[(int64_t)i * half + (first ? d : d - half)];
+        const float xp = rowbuf[wave][first ? d + half : d - half];
+        x[e] = first ? (x[e] * cs.x + xp * cs.y) : (x[e] * cs.x - xp * cs.y);
+      }
+    }
   }
   if (out_f32) {
     float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
@@ -358,65 +593,42 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f
   }
 }
 
-template <int D, int ROT>
-hipError_t launch_main(const BwdParams& p, hipStream_t st) {
-  const int nkt = (p.a.S + BNK - 1) / BNK;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, ROT>), dim3((unsigned)(nkt * p.a.B * p.a.H)), dim3(NT), 0,
-                     st, p);
-  return hipGetLastError();
-}
-
 template <int D>
-hipError_t launch_main_rot(const BwdParams& p, hipStream_t st) {
-  if (p.a.rd == 0) return launch_main<D, 0>(p, st);
-  if (p.a.rd % 8 == 0) return launch_main<D, 1>(p, st);
-  return launch_main<D, 2>(p, st);
+hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+  hipError_t e;
+  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+  const dim3 row_grid((unsigned)((rows + 3) / 4));
+  if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid, dim3(256), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
+  const int nkt = (p.a.S + BNK - 1) / BNK;
+  const dim3 grid((unsigned)(nkt * p.a.B * p.a.H));
+  if (p.a.alibi)
+    hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_finalize_kernel<D>), row_grid, dim3(256), 0, st, p, p.out_f32);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record_event(ev, 3, st);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
-  hipError_t e;
-  if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  if ((e = launch_bwd_pre(p, st, false)) != hipSuccess) return e;
-  if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
   switch (p.a.D) {
-    case 64: e = launch_main_rot<64>(p, st); break;
-    case 96: e = launch_main_rot<96>(p, st); break;
-    case 128: e = launch_main_rot<128>(p, st); break;
+    case 64: return launch_d<64>(p, st, ev);
+    case 96: return launch_d<96>(p, st, ev);
+    case 128: return launch_d<128>(p, st, ev);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  if ((e = launch_dq_finalize(p, st, p.out_f32)) != hipSuccess) return e;
-  return record_event(ev, 3, st);
-}
-
-// fp32 storage shares the preprocess and finalize kernels (see bwd_f32.hip).
-hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t st, bool f32) {
-  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-  const dim3 grid((unsigned)((rows + 15) / 16));
-  switch (p.a.D) {
-    case 64:
-      if (f32) hipLaunchKernelGGL((bwd_pre_kernel<64, true>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((bwd_pre_kernel<64, false>), grid, dim3(256), 0, st, p);
-      break;
-    case 96:
-      if (f32) hipLaunchKernelGGL((bwd_pre_kernel<96, true>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((bwd_pre_kernel<96, false>), grid, dim3(256), 0, st, p);
-      break;
-    case 128:
-      if (f32) hipLaunchKernelGGL((bwd_pre_kernel<128, true>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((bwd_pre_kernel<128, false>), grid, dim3(256), 0, st, p);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32) {
-  const int64_t items = (int64_t)p.a.B * p.a.H * p.a.S * (p.a.D / 8);
-  const dim3 grid((unsigned)((items + 255) / 256));
+  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+  const dim3 grid((unsigned)((rows + 3) / 4));
   switch (p.a.D) {
     case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), grid, dim3(256), 0, st, p, out_f32); break;
     case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), grid, dim3(256), 0, st, p, out_f32); break;

@@ -32,6 +32,28 @@ __device__ __forceinline__ float rot_elem(const float* row, int d, int pos, int 
   return x * cs.x + row[d - half] * cs.y;
 }
 
+// Delta_i = dO_i . o_i and a zeroed dq accumulator row; one wave per row.
+template <int D>
+__global__ __launch_bounds__(256) void pre_f32_kernel(BwdParams p) {
+  const int S = p.a.S;
+  const int64_t rows = (int64_t)p.a.B * p.a.H * S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const int bh = (int)(r / S), i = (int)(r % S);
+  const int b = bh / p.a.H, h = bh % p.a.H;
+  const float* orow = (const float*)p.o + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s;
+  const float* grow = (const float*)p.dout + b * p.sdo.b + h * p.sdo.h + (int64_t)i * p.sdo.s;
+  float sum = 0.0f;
+  for (int d = lane; d < D; d += 64) {
+    sum = fmaf(orow[d], grow[d], sum);
+    p.dq_acc[r * D + d] = 0.0f;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if (lane == 0) p.delta[r] = sum;
+}
+
 __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
@@ -251,7 +273,14 @@ hipError_t launch_main(const BwdParams& p, hipStream_t st) {
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
   if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  if ((e = launch_bwd_pre(p, st, true)) != hipSuccess) return e;
+  const dim3 row_grid((unsigned)(((int64_t)p.a.B * p.a.H * p.a.S + 3) / 4));
+  switch (p.a.D) {
+    case 64: hipLaunchKernelGGL((pre_f32_kernel<64>), row_grid, dim3(256), 0, st, p); break;
+    case 96: hipLaunchKernelGGL((pre_f32_kernel<96>), row_grid, dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((pre_f32_kernel<128>), row_grid, dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
   switch (p.a.D) {
     case 64: e = launch_main<64>(p, st); break;

@@ -16,13 +16,14 @@
 //  * O^T += V^T P^T: B = P straight from the score registers; A = V^T read from
 //    the row-major V tile with ds_read_b64_tr_b16 (two 4-key reads per 8-key
 //    operand), so V needs no transposition anywhere.
-//  * Software pipeline: the next tile's K/V rows are fetched into registers
-//    while the current tile is computed from LDS, then rotated/stored into the
-//    other LDS buffer; one barrier per tile.
-//  * Tiles that need no mask (fully inside every row's allowed range) run a
-//    mask-free softmax; the running max is raised lazily (only when a row's
-//    max grows by more than 2^8 in the exp2 domain), so O and the row sum are
-//    rescaled rarely.
+//  * K/V tiles go global -> LDS directly (global_load_lds_dwordx4) into an
+//    unpadded, XOR-swizzled layout that keeps the operand reads free of bank
+//    conflicts; only the rotary dims of K pass through registers.  Two LDS
+//    buffers, one barrier per tile; every LDS operand address is a per-lane
+//    register (moved by one tile when the buffers swap) plus an immediate.
+//  * Tiles fully inside every row's allowed range skip the mask; the running
+//    max is raised lazily (only when a row's max grows by more than 2^8 in the
+//    exp2 domain), so O and the row sum are rescaled rarely.
 //  * Workgroups are issued heaviest q-tile first, heads fastest: with B*H a
 //    multiple of 8 all q-tiles of a head share one XCD and its L2.
 #include "device_common.hpp"
@@ -63,12 +64,13 @@ struct Swz {
 };
 
 // Per-thread plan for staging one K/V tile.  V, and the K chunks outside the
-// rotary dims, go global -> LDS directly (global_load_lds_dwordx4: lane l of a
-// wave writes position 64*block + l, so each lane fetches the global chunk
-// that belongs at that position).  The rotary K dims go through registers as
-// "pair items" (row, W consecutive pairs: dims p0.. and half+p0..) and are
-// rotated before being written to LDS; for rotary widths that are not a
-// multiple of 8 every K chunk goes through registers (rotated element-wise).
+// rotary dims, go global -> LDS directly (lane l of a wave writes position
+// 64*block + l, so each lane fetches the global chunk that belongs there;
+// offsets are 32-bit element offsets from the tile's first row).  The rotary
+// K dims go through registers as "pair items" (row, W consecutive pairs: dims
+// p0.. and half+p0..) and are rotated before being written to LDS; for rotary
+// widths that are not a multiple of 8 every K chunk goes through registers
+// (rotated element-wise).
 template <int D, int ROT>
 struct TilePlan {
   static constexpr int CPR = D / 8;             // chunks per row
@@ -77,28 +79,31 @@ struct TilePlan {
   static constexpr int W = ROT == 1 ? 8 : 4;    // pairs per pair item
   static constexpr int NPAIR = PAIRS ? (BN * D / (2 * W) + NT - 1) / NT : 1;
   static constexpr int NREG = ROT == 3 ? BN * CPR / NT : 1;
-  int kpos[NB];   // row << 8 | chunk of this lane's K position in block i (chunk -1: not direct)
-  int vpos[NB];
-  int pitem[NPAIR];            // row << 8 | p0, -1 unused
-  int plds[NPAIR];             // LDS element offset of dims p0.. (low 16) and half+p0.. (high 16)
+  int kdirect;            // bit i: this lane's K position of block i is loaded directly
+  int koff[NB], voff[NB]; // row * stride + 8 * chunk
+  int pitem[NPAIR];       // row << 8 | p0, -1 unused
+  int plds[NPAIR];        // LDS element offsets of dims p0.. (low 16 bits) and half+p0..
   u32x4 plo[NPAIR], phi[NPAIR];
-  int ritem[NREG];             // ROT 3: row << 8 | chunk
+  int ritem[NREG];        // ROT 3: row << 8 | chunk
   u32x4 rk[NREG];
 
   __device__ __forceinline__ static int kp(int row, int chunk) {
     return row * CPR + (chunk ^ Swz<D>::k(row));
   }
 
-  __device__ __forceinline__ void init(int wave, int lane, int tid, int rd) {
+  __device__ __forceinline__ void init(int wave, int lane, int tid, int rd, int64_t ks,
+                                       int64_t vs) {
     const int rchunks = PAIRS ? rd / 8 : (ROT == 3 ? CPR : 0);  // K chunks not loaded directly
+    kdirect = 0;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int P = 64 * (wave + 4 * i) + lane;
       const int row = P / CPR;
       const int ck = (P % CPR) ^ Swz<D>::k(row);
       const int cv = (P % CPR) ^ Swz<D>::v(row);
-      kpos[i] = ck < rchunks ? -1 : (row << 8) | ck;
-      vpos[i] = (row << 8) | cv;
+      if (ck >= rchunks) kdirect |= 1 << i;
+      koff[i] = (int)(row * ks) + 8 * ck;
+      voff[i] = (int)(row * vs) + 8 * cv;
     }
     const int half = rd >> 1;
     const int slots = PAIRS ? half / W : 0;
@@ -128,19 +133,27 @@ struct TilePlan {
   __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, int64_t ks,
                                         const uint16_t* __restrict__ vb, int64_t vs, int k0,
                                         int S, int rd, uint16_t* Kt, uint16_t* Vt, int wave) {
-    const bool full = k0 + BN <= S;
+    if (k0 + BN <= S) {
+      const uint16_t* kt0 = kb + (int64_t)k0 * ks;
+      const uint16_t* vt0 = vb + (int64_t)k0 * vs;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int blk = wave + 4 * i;
-      {
-        const int row = vpos[i] >> 8, c = vpos[i] & 255;
-        const int r = full ? k0 + row : min(k0 + row, S - 1);
-        load_lds16(vb + (int64_t)r * vs + 8 * c, Vt + 512 * blk);
+      for (int i = 0; i < NB; ++i) {
+        const int blk = wave + 4 * i;
+        load_lds16(vt0 + voff[i], Vt + 512 * blk);
+        if (kdirect & (1 << i)) load_lds16(kt0 + koff[i], Kt + 512 * blk);
       }
-      if (kpos[i] >= 0) {
-        const int row = kpos[i] >> 8, c = kpos[i] & 255;
-        const int r = full ? k0 + row : min(k0 + row, S - 1);
-        load_lds16(kb + (int64_t)r * ks + 8 * c, Kt + 512 * blk);
+    } else {
+      // last tile: rows past S re-read row S-1 (their keys are masked)
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int blk = wave + 4 * i;
+        const int P = 64 * blk + lane;
+        const int row = P / CPR;
+        const int r = min(k0 + row, S - 1);
+        load_lds16(vb + (int64_t)r * vs + 8 * ((P % CPR) ^ Swz<D>::v(row)), Vt + 512 * blk);
+        if (kdirect & (1 << i))
+          load_lds16(kb + (int64_t)r * ks + 8 * ((P % CPR) ^ Swz<D>::k(row)), Kt + 512 * blk);
       }
     }
     const int half = rd >> 1;
@@ -149,7 +162,7 @@ struct TilePlan {
       for (int i = 0; i < NPAIR; ++i) {
         if (pitem[i] >= 0) {
           const int row = pitem[i] >> 8, p0 = pitem[i] & 255;
-          const int r = full ? k0 + row : min(k0 + row, S - 1);
+          const int r = min(k0 + row, S - 1);
           const uint16_t* src = kb + (int64_t)r * ks + p0;
           if (W == 8) {
             plo[i] = *reinterpret_cast<const u32x4*>(src);
@@ -227,124 +240,46 @@ struct TilePlan {
   }
 };
 
+// State of one workgroup's forward pass (one wave's view).
 template <int D, int ROT, bool ALIBI>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int CPR = D / 8;
-  constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
-
-  const AttnShape& a = p.a;
-  const int S = a.S;
-  const int nqt = (S + BM - 1) / BM;
-  const int BH = a.B * a.H;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ql = lane & 31, hh = lane >> 5;
-  const int q0 = qt * BM;
-  const int qi = q0 + wave * 32 + ql;  // this lane's query row
-
-  const uint16_t* qb = (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* kb = (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
-  const uint16_t* vb = (const uint16_t*)p.v + b * p.sv.b + h * p.sv.h;
-
-  // Allowed keys of this lane's query: [lo, hi].
-  const int32_t* drow = a.docs ? a.docs + (int64_t)b * (a.n_docs + 1) : nullptr;
-  const int qc = qi < S ? qi : S - 1;
-  int lo = 0, hi = S - 1;
-  if (drow) {
-    int ds, de;
-    doc_bounds(drow, a.n_docs, S, qc, ds, de);
-    lo = ds;
-    hi = de - 1;
-  }
-  if (a.causal && qi < hi) hi = qi;
-  // Keys any query of the workgroup may see.
-  const int qlast = (q0 + BM - 1 < S - 1) ? q0 + BM - 1 : S - 1;
-  int blo = 0, bhi = S - 1;
-  if (drow) {
-    int s0, e0, s1, e1;
-    doc_bounds(drow, a.n_docs, S, q0, s0, e0);
-    doc_bounds(drow, a.n_docs, S, qlast, s1, e1);
-    blo = s0;
-    bhi = e1 - 1;
-  }
-  if (a.causal && qlast < bhi) bhi = qlast;
-  const int kt_lo = blo / BN, kt_hi = bhi / BN + 1;
-
-  // Prologue: fetch the first tile while Q~ is being loaded.
+struct FwdState {
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BN * D;
+  uint16_t* lds;
   TilePlan<D, ROT> tp;
-  tp.init(wave, lane, tid, a.rd);
-  tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + 2 * TILE, wave);
-
-  // Q~ of this lane's row as the B operand: chunk c holds dims 16c + 8hh .. +7.
   bf16x8 qreg[D / 16];
-  {
-    const uint16_t* qrow = qb + (int64_t)qc * p.sq.s;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const int d0 = 16 * c + 8 * hh;
-      float x[8];
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf_lo(w[e]);
-        x[2 * e + 1] = bf_hi(w[e]);
-      }
-      if (ROT != 0) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
-      if (qi >= S) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-      }
-      qreg[c] = pack8(x);
-    }
-  }
-  tp.store(lds, kb, p.sk.s, kt_lo * BN, S, a.rd, a.rope);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  const float sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
-  const float c2 = a.scale_log2;
-  float m_ref = -INFINITY;  // running max in the exp2 domain (raised lazily)
-  float l_run = 0.0f;       // this lane's partial row sum (its 16 keys per block)
   f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_ref, l_run;
+  // LDS element offsets (from lds) of this lane's operand reads in the current
+  // buffer; they move by +-TILE when the buffers swap.
+  int kaddr[D / 16];     // K~ A operand, rows 0..31 (per chunk pair); rows 32..63
+                         // use the same swizzle, 32 * D elements further
+  int vaddr[D / 32];     // V^T transposed reads (per dim block)
+  int bdelta;            // +TILE or -TILE: move to the other buffer
+  int lo, hi, qi, hh, wave;
+  float c2, sl2;
 
-  // Per-lane LDS operand addressing.  K~ A operand: row ql (+32 per block),
-  // chunk 2c + hh.  V^T via transposed reads: lane 16g + j reads 4 dims
-  // (chunk 4 db + 2 (g&1) + (j&3)/2, half (j&1)) of key 16 cp + 4 hh + j/4 (+8).
-  const int krow0 = ql * CPR, krow1 = (32 + ql) * CPR;
-  const int ksw0 = Swz<D>::k(ql), ksw1 = Swz<D>::k(32 + ql);
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int vkey = 4 * hh + (j16 >> 2);
-  const int vsw = Swz<D>::v(vkey);  // same for keys vkey + 16 cp and vkey + 8
-  const int vch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  const int vhalf = 4 * (j16 & 1);
-
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+  // One 64-key tile read from LDS buffer `buf`; fetches the next tile (if any)
+  // into the other buffer meanwhile.
+  __device__ __forceinline__ void step(const FwdParams& p, const uint16_t* kb,
+                                       const uint16_t* vb, int kt, int kt_hi, int buf) {
+    const AttnShape& a = p.a;
+    const int S = a.S;
     const int k0 = kt * BN;
-    const int buf = (kt - kt_lo) & 1;
-    const uint16_t* Kc = lds + buf * TILE;
-    const uint16_t* Vc = lds + (2 + buf) * TILE;
+    uint16_t* Kn = lds + (1 - buf) * TILE;
+    uint16_t* Vn = lds + (3 - buf) * TILE;
     const bool more = kt + 1 < kt_hi;
-    if (more)
-      tp.fetch(kb, p.sk.s, vb, p.sv.s, k0 + BN, S, a.rd, lds + (buf ^ 1) * TILE,
-               lds + (2 + (buf ^ 1)) * TILE, wave);
+    if (more) tp.fetch(kb, p.sk.s, vb, p.sv.s, k0 + BN, S, a.rd, Kn, Vn, wave);
 
     const bool lane_any = (k0 <= hi) && (k0 + BN - 1 >= lo);
     if (__any(lane_any)) {
       const bool lane_full = (k0 >= lo) && (k0 + BN - 1 <= hi);
       const bool need_mask = !__all(lane_full);
-
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 ka0 = lds_read8(Kc + 8 * (krow0 + ((2 * c + hh) ^ ksw0)));
-        const bf16x8 ka1 = lds_read8(Kc + 8 * (krow1 + ((2 * c + hh) ^ ksw1)));
-        sacc[0] = mfma32x32x16(ka0, qreg[c], sacc[0]);
-        sacc[1] = mfma32x32x16(ka1, qreg[c], sacc[1]);
+        sacc[0] = mfma32x32x16(lds_read8(lds + kaddr[c]), qreg[c], sacc[0]);
+        sacc[1] = mfma32x32x16(lds_read8(lds + kaddr[c] + 32 * D), qreg[c], sacc[1]);
       }
       // Register r of block blk: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.  The
       // scores stay in the accumulator registers: raw (RoPE) or exp2-domain
@@ -392,7 +327,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
           sacc[blk][r] = ALIBI ? fast_exp2(x - m_use) : fast_exp2(__builtin_fmaf(x, c2, -m_use));
           l_run += sacc[blk][r];
         }
-
 #pragma unroll
       for (int cp = 0; cp < BN / 16; ++cp) {
         float pv[8];
@@ -401,8 +335,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
         const bf16x8 pb = pack8(pv);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int vc = (4 * db + vch) ^ vsw;
-          const uint16_t* vp = Vc + 8 * ((16 * cp + vkey) * CPR + vc) + vhalf;
+          const uint16_t* vp = lds + vaddr[db] + 16 * cp * 8 * CPR;
           const s16x4 v0 = lds_read_tr4(vp);
           const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
           const bf16x8 va = __builtin_bit_cast(
@@ -411,16 +344,128 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    if (more) tp.store(lds + (buf ^ 1) * TILE, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
+    if (more) tp.store(Kn, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kaddr[c] += bdelta;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) vaddr[db] += bdelta;
+    bdelta = -bdelta;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+};
+
+template <int D, int ROT, bool ALIBI>
+__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
+
+  const AttnShape& a = p.a;
+  const int S = a.S;
+  const int nqt = (S + BM - 1) / BM;
+  const int BH = a.B * a.H;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int q0 = qt * BM;
+
+  FwdState<D, ROT, ALIBI> st;
+  st.lds = lds;
+  st.wave = wave;
+  st.hh = hh;
+  st.qi = q0 + wave * 32 + ql;  // this lane's query row
+  const int qi = st.qi;
+
+  const uint16_t* qb = (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
+  const uint16_t* kb = (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
+  const uint16_t* vb = (const uint16_t*)p.v + b * p.sv.b + h * p.sv.h;
+
+  // Allowed keys of this lane's query: [lo, hi].
+  const int32_t* drow = a.docs ? a.docs + (int64_t)b * (a.n_docs + 1) : nullptr;
+  const int qc = qi < S ? qi : S - 1;
+  st.lo = 0;
+  st.hi = S - 1;
+  if (drow) {
+    int ds, de;
+    doc_bounds(drow, a.n_docs, S, qc, ds, de);
+    st.lo = ds;
+    st.hi = de - 1;
+  }
+  if (a.causal && qi < st.hi) st.hi = qi;
+  // Keys any query of the workgroup may see.
+  const int qlast = (q0 + BM - 1 < S - 1) ? q0 + BM - 1 : S - 1;
+  int blo = 0, bhi = S - 1;
+  if (drow) {
+    int s0, e0, s1, e1;
+    doc_bounds(drow, a.n_docs, S, q0, s0, e0);
+    doc_bounds(drow, a.n_docs, S, qlast, s1, e1);
+    blo = s0;
+    bhi = e1 - 1;
+  }
+  if (a.causal && qlast < bhi) bhi = qlast;
+  const int kt_lo = blo / BN, kt_hi = bhi / BN + 1;
+
+  // Prologue: fetch the first tile while Q~ is being loaded.
+  st.tp.init(wave, lane, tid, a.rd, p.sk.s, p.sv.s);
+  st.tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + 2 * TILE, wave);
+
+  // Q~ of this lane's row as the B operand: chunk c holds dims 16c + 8hh .. +7.
+  {
+    const uint16_t* qrow = qb + (int64_t)qc * p.sq.s;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const int d0 = 16 * c + 8 * hh;
+      float x[8];
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf_lo(w[e]);
+        x[2 * e + 1] = bf_hi(w[e]);
+      }
+      if (ROT != 0) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
+      if (qi >= S) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+      }
+      st.qreg[c] = pack8(x);
+    }
+  }
+  // LDS operand offsets.  K~ A operand: row ql (+32 per block), chunk 2c + hh.
+  // V^T via transposed reads: lane 16g + j reads 4 dims (chunk 4 db + 2 (g&1) +
+  // (j&3)/2, half (j&1)) of key 16 cp + 4 hh + j/4 (+8).
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) st.kaddr[c] = 8 * (ql * CPR + ((2 * c + hh) ^ Swz<D>::k(ql)));
+  st.bdelta = TILE;
+  {
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int vkey = 4 * hh + (j16 >> 2);
+    const int vsw = Swz<D>::v(vkey);  // same for keys vkey + 16 cp and vkey + 8
+    const int vch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      st.vaddr[db] = 2 * TILE + 8 * (vkey * CPR + ((4 * db + vch) ^ vsw)) + 4 * (j16 & 1);
+  }
+  st.tp.store(lds, kb, p.sk.s, kt_lo * BN, S, a.rd, a.rope);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  st.sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
+  st.c2 = a.scale_log2;
+  st.m_ref = -INFINITY;  // running max in the exp2 domain (raised lazily)
+  st.l_run = 0.0f;       // this lane's partial row sum (its 16 keys per block)
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.oacc[db] = f32x16{};
+
+  for (int kt = kt_lo; kt < kt_hi; ++kt) st.step(p, kb, vb, kt, kt_hi, (kt - kt_lo) & 1);
 
   // Epilogue: o = O / l, lse = (m + log2 l) ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
   const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qi < S) {
-    if (hh == 0) p.lse[(int64_t)bh * S + qi] = (m_ref + __log2f(l_tot)) * kLn2;
+    if (hh == 0) p.lse[(int64_t)bh * S + qi] = (st.m_ref + __log2f(l_tot)) * kLn2;
     // Register r of block db holds dim 32 db + 8 (r/4) + 4 hh + r%4.
     if (p.out_f32) {
       float* orow = (float*)p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s;
@@ -430,7 +475,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
         for (int a4 = 0; a4 < 4; ++a4) {
           f32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * a4 + e] * inv_l;
+          for (int e = 0; e < 4; ++e) w[e] = st.oacc[db][4 * a4 + e] * inv_l;
           *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a4 + 4 * hh) = w;
         }
     } else {
@@ -440,8 +485,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           u32x2 w;
-          w[0] = pack2(oacc[db][4 * a4] * inv_l, oacc[db][4 * a4 + 1] * inv_l);
-          w[1] = pack2(oacc[db][4 * a4 + 2] * inv_l, oacc[db][4 * a4 + 3] * inv_l);
+          w[0] = pack2(st.oacc[db][4 * a4] * inv_l, st.oacc[db][4 * a4 + 1] * inv_l);
+          w[1] = pack2(st.oacc[db][4 * a4 + 2] * inv_l, st.oacc[db][4 * a4 + 3] * inv_l);
           *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hh) = w;
         }
     }

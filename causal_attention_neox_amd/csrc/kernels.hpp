@@ -48,10 +48,13 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // [B][H][S][D] fp32 workspace (contiguous)
-  float* delta;   // [B][H][S] fp32 workspace
+  float* dq_acc;   // [B][H][S][D] fp32 workspace (contiguous)
+  float* delta;    // [B][H][S] fp32 workspace: dO_i . o_i
+  float* nlse;     // [B][H][S] fp32 workspace: -lse_i * log2(e) (ALiBi: also - slope * log2(e) * i)
+  uint16_t* qrot;  // [B][H][S][D] bf16 workspace: rotated q (bf16 path with rotary)
+  uint16_t* krot;  // [B][H][S][D] bf16 workspace: rotated k
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
-  int out_f32;    // dq, dk, dv stored as fp32
+  int out_f32;     // dq, dk, dv stored as fp32
 };
 
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
@@ -64,8 +67,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 
-// Preprocess (Delta, zeroed dq accumulator) and dq finalize, shared by both paths.
-hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t st, bool f32);
+// dq = R^T dQ~ from the fp32 accumulator, cast; shared by both paths.
 hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32);
 
 inline hipError_t record_event(const hipEvent_t* ev, int i, hipStream_t st) {

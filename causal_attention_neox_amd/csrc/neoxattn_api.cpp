@@ -168,9 +168,40 @@ int prepare_rope(const neox_attn_args* a, int dev, hipStream_t st, const float2*
   return NEOX_OK;
 }
 
+// Backward workspace: fp32 dq accumulator [rows][D], fp32 Delta [rows], fp32
+// -lse*log2e [rows], and the rotated bf16 q and k [rows][D] each; 256-byte
+// aligned pieces, rows = B*H*S.
+struct BwdWorkspace {
+  size_t dq_acc, delta, nlse, qrot, krot, total;
+};
+
+bool bwd_workspace_layout(int B, int H, int S, int D, BwdWorkspace* w) {
+  if (B < 1 || H < 1 || S < 1 || D < 1) return false;
+  const int64_t rows = (int64_t)B * H * S;
+  if (rows >= kMaxRows || D > 4096) return false;
+  size_t off = 0;
+  w->dq_acc = off;
+  off += round256((size_t)rows * (size_t)D * 4u);
+  w->delta = off;
+  off += round256((size_t)rows * 4u);
+  w->nlse = off;
+  off += round256((size_t)rows * 4u);
+  w->qrot = off;
+  off += round256((size_t)rows * (size_t)D * 2u);
+  w->krot = off;
+  off += round256((size_t)rows * (size_t)D * 2u);
+  w->total = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D) {
+  BwdWorkspace w;
+  return bwd_workspace_layout(B, H, S, D, &w) ? w.total : 0;
+}
 
 const char* neox_status_str(int status) {
   switch (status) {
@@ -184,13 +215,6 @@ const char* neox_status_str(int status) {
     case NEOX_E_ALLOC: return "rotary table allocation failed or not prepared under capture";
     default: return "unknown status";
   }
-}
-
-size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D) {
-  if (B < 1 || H < 1 || S < 1 || D < 1) return 0;
-  const int64_t rows = (int64_t)B * H * S;
-  if (rows >= kMaxRows || D > 4096) return 0;
-  return round256((size_t)rows * (size_t)D * 4u) + round256((size_t)rows * 4u);
 }
 
 int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, const void* v,
@@ -275,10 +299,14 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  const int64_t rows = (int64_t)a->B * a->H * a->S;
-  p.dq_acc = reinterpret_cast<float*>(workspace);
-  p.delta = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                     round256((size_t)rows * (size_t)a->D * 4u));
+  BwdWorkspace wl;
+  bwd_workspace_layout(a->B, a->H, a->S, a->D, &wl);
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.dq_acc = reinterpret_cast<float*>(ws + wl.dq_acc);
+  p.delta = reinterpret_cast<float*>(ws + wl.delta);
+  p.nlse = reinterpret_cast<float*>(ws + wl.nlse);
+  p.qrot = reinterpret_cast<uint16_t*>(ws + wl.qrot);
+  p.krot = reinterpret_cast<uint16_t*>(ws + wl.krot);
   p.sq = to_internal(s ? s[0] : def);
   p.sk = to_internal(s ? s[1] : def);
   p.sv = to_internal(s ? s[2] : def);

@@ -141,9 +141,12 @@ int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int S, int D, int rotary_dim, float rope_base,
                        int causal, float softmax_scale, int dtype, void* stream);
 
-/* Bytes of device workspace the backward needs: an fp32 [B, H, S, D] dq
- * accumulator and an fp32 [B, H, S] row term, each 256-byte aligned.  Returns
- * 0 for sizes that are invalid (<= 0) or overflow. */
+/* Bytes of device workspace the backward needs, in five 256-byte aligned
+ * parts: an fp32 [B, H, S, D] dq accumulator, two fp32 [B, H, S] row terms
+ * (the softmax-gradient row sum and the negated base-2 log-sum-exp), and the
+ * rotated q and k as bf16, [B, H, S, D] each (used by the bf16 path only; the
+ * size does not depend on dtype) -- B*H*S*(8D + 8) bytes up to rounding,
+ * linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
 size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
 
 /*

@@ -157,12 +157,15 @@ def test_valid_call_without_gpu_fails_loudly(lib):
 
 
 def test_workspace_size_is_linear_in_sequence_length(lib):
-    """O(n) memory: the backward workspace is B*H*S*(D+1)*4 bytes up to
-    256-byte rounding, with no S^2 term."""
+    """O(n) memory: the backward workspace is an fp32 dq accumulator, two fp32
+    row terms and the rotated q and k (2 bytes per element), each part rounded
+    up to 256 bytes, with no S^2 term."""
+    def r256(n):
+        return ((n + 255) // 256) * 256
     for (B, H, D) in [(1, 1, 64), (4, 64, 96), (1, 32, 128)]:
         for S in (1, 17, 2048, 16384, 1 << 20):
             rows = B * H * S
-            expect = ((rows * D * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+            expect = r256(rows * D * 4) + 2 * r256(rows * 4) + 2 * r256(rows * D * 2)
             assert lib.neox_rope_attn_bwd_workspace_size(B, H, S, D) == expect
     assert lib.neox_rope_attn_bwd_workspace_size(0, 1, 1, 64) == 0
     assert lib.neox_rope_attn_bwd_workspace_size(1 << 16, 1 << 8, 1 << 8, 64) == 0
