@@ -202,9 +202,12 @@ def main():
     kern = {
         "fwd": dict(flops=fwd_flops, ms=kms["fwd"], bound="mfma"),
         "bwd_main": dict(flops=bwd_flops, ms=kms["bwd_main"], bound="mfma"),
-        # preprocess: reads o and dO, writes Delta and the zeroed fp32 dq accumulator
-        "bwd_pre": dict(bytes=rows * wl.D * (2 * el + 4) + rows * 4, ms=kms["bwd_pre"],
-                        bound="hbm"),
+        # preprocess: reads o, dO and lse, writes Delta, the row log-sum-exp term and
+        # the zeroed fp32 dq accumulator; with rotary it also reads q, k and writes
+        # the rotated copies (bf16)
+        "bwd_pre": dict(bytes=rows * wl.D * (2 * el + 4) + rows * 12
+                        + (rows * wl.D * (2 * el + 4) if wl.rotary_dim > 0 and el == 2 else 0),
+                        ms=kms["bwd_pre"], bound="hbm"),
         # finalize: reads the fp32 dq accumulator, writes dq
         "bwd_dq_finalize": dict(bytes=rows * wl.D * (4 + el), ms=kms["bwd_dq_finalize"],
                                 bound="hbm"),

@@ -71,84 +71,122 @@ __device__ __forceinline__ int tpos(int row, int chunk) {
 
 // ------------------------------------------------------------------------ prep
 
-// One wave per row, 16 B per lane: lanes 0..D/8-1 of the wave hold chunks of
-// q, k, o, dO of the row.  The rotary partners (dims +- rd/2) are exchanged
-// through a per-wave LDS row.
+// The per-row passes (prep, finalize) give each row a group of G lanes, G =
+// D/8 rounded up to a power of two, 16 B per lane, so one wave covers 64/G
+// rows and every memory instruction is full width.  Each lane issues all of
+// its loads before it uses any, and rotary partners (dims +- rd/2, which need
+// not fall on 8-dim chunk boundaries) are exchanged through LDS behind an
+// LDS-only wait, so outstanding stores never stall the exchange.
+template <int D>
+struct RowGroups {
+  static constexpr int C = D / 8;
+  static constexpr int G = C <= 8 ? 8 : 16;
+  static constexpr int RPW = 64 / G;  // rows per wave
+  static constexpr int RPB = 4 * RPW; // rows per 256-thread workgroup
+};
+
+// Waits for this wave's LDS operations only (lgkmcnt(0); vmcnt and expcnt
+// left at their maxima in the gfx9 s_waitcnt encoding).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  constexpr int C = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][2][D];
+  using RG = RowGroups<D>;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW;
+  __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][RPW][2][D];
   const AttnShape& a = p.a;
-  const int S = a.S;
-  const int64_t rows = (int64_t)a.B * a.H * S;
+  const int S = a.S, rd = a.rd, half = rd >> 1;
+  const int rows = a.B * a.H * S;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  if (r >= rows) return;  // whole waves only
-  const int bh = (int)(r / S), i = (int)(r % S);
-  const int b = bh / a.H, h = bh % a.H;
-  const bool act = lane < C;
-  const int d0 = 8 * lane;
-  float sum = 0.0f;
+  const int g = lane & (G - 1), rw = lane / G;
+  const int wrow0 = (blockIdx.x * 4 + wave) * RPW;
+  if (wrow0 >= rows) return;  // whole waves only
+  const int r = wrow0 + rw;
+  const bool act = r < rows && g < C;
+  const int bh = r / S, i = r - bh * S;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int d0 = 8 * g;
+  const bool rot_lane = act && d0 < rd;
+
+  u32x4 ow = u32x4{0u, 0u, 0u, 0u}, gw = ow, qw = ow, kw = ow;
+  float lse = 0.0f;
+  float2 cs[8];
   if (act) {
-    const u32x4 ow = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b +
-                                                     h * p.so.h + (int64_t)i * p.so.s + d0);
-    const u32x4 gw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b +
-                                                     h * p.sdo.h + (int64_t)i * p.sdo.s + d0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sum = fmaf(bf_lo(ow[e]), bf_lo(gw[e]), sum);
-      sum = fmaf(bf_hi(ow[e]), bf_hi(gw[e]), sum);
+    ow = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b + h * p.so.h +
+                                         (int64_t)i * p.so.s + d0);
+    gw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h +
+                                         (int64_t)i * p.sdo.s + d0);
+    if (rd > 0) {
+      qw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
+                                           (int64_t)i * p.sq.s + d0);
+      kw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
+                                           (int64_t)i * p.sk.s + d0);
     }
-    float* acc = p.dq_acc + r * D + d0;
+    if (g == 0) lse = p.lse[r];
+  }
+  if (rot_lane) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      cs[e] = d < rd ? a.rope[(int64_t)i * half + (d < half ? d : d - half)] : float2{1.0f, 0.0f};
+    }
+  }
+
+  float sum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sum = fmaf(bf_lo(ow[e]), bf_lo(gw[e]), sum);
+    sum = fmaf(bf_hi(ow[e]), bf_hi(gw[e]), sum);
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if (act) {
+    float* acc = p.dq_acc + (int64_t)r * D + d0;
     *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (g == 0) {
+      p.delta[r] = sum;
+      float nl = -lse * kLog2e;
+      if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)i;
+      p.nlse[r] = nl;
+    }
   }
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-  if (lane == 0) {
-    p.delta[r] = sum;
-    float nl = -p.lse[r] * kLog2e;
-    if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)i;
-    p.nlse[r] = nl;
-  }
-  const int rd = a.rd;
   if (rd == 0) return;
-  const int half = rd >> 1;
+
+  if (act) {
+    *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][0][d0]) = qw;
+    *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][1][d0]) = kw;
+  }
+  lds_wave_sync();
+  if (rot_lane) {
+    float xq[8], xk[8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint16_t* src = t == 0 ? (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h + (int64_t)i * p.sq.s
-                                 : (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h + (int64_t)i * p.sk.s;
-    uint16_t* dst = (t == 0 ? p.qrot : p.krot) + r * D + d0;
-    u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (act) {
-      w = *reinterpret_cast<const u32x4*>(src + d0);
-      *reinterpret_cast<u32x4*>(&rowbuf[wave][t][d0]) = w;
+    for (int e = 0; e < 4; ++e) {
+      xq[2 * e] = bf_lo(qw[e]);
+      xq[2 * e + 1] = bf_hi(qw[e]);
+      xk[2 * e] = bf_lo(kw[e]);
+      xk[2 * e + 1] = bf_hi(kw[e]);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
-    if (act) {
-      if (d0 < rd) {
-        float x[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf_lo(w[e]);
-          x[2 * e + 1] = bf_hi(w[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = d0 + e;
-          if (d < rd) {
-            const bool first = d < half;
-            const int pp = first ? d : d - half;
-            const float xp = bf2f(rowbuf[wave][t][first ? d + half : d - half]);
-            const float2 cs = a.rope[(int64_t)i * half + pp];
-            x[e] = first ? (x[e] * cs.x - xp * cs.y) : (x[e] * cs.x + xp * cs.y);
-          }
-        }
-        w = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      if (d < rd) {
+        const bool first = d < half;
+        const int pd = first ? d + half : d - half;
+        const float sn = first ? -cs[e].y : cs[e].y;  // rotate-half: (-x2, x1)
+        xq[e] = fmaf(bf2f(rowbuf[wave][rw][0][pd]), sn, xq[e] * cs[e].x);
+        xk[e] = fmaf(bf2f(rowbuf[wave][rw][1][pd]), sn, xk[e] * cs[e].x);
       }
-      *reinterpret_cast<u32x4*>(dst) = w;
     }
+    qw = u32x4{pack2(xq[0], xq[1]), pack2(xq[2], xq[3]), pack2(xq[4], xq[5]), pack2(xq[6], xq[7])};
+    kw = u32x4{pack2(xk[0], xk[1]), pack2(xk[2], xk[3]), pack2(xk[4], xk[5]), pack2(xk[6], xk[7])};
+  }
+  if (act) {
+    *reinterpret_cast<u32x4*>(p.qrot + (int64_t)r * D + d0) = qw;
+    *reinterpret_cast<u32x4*>(p.krot + (int64_t)r * D + d0) = kw;
   }
 }
 
@@ -535,53 +573,66 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ finalize
 
-// dq = R^T dQ~ (rotation by -theta), cast to the output type.  One wave per
-// row, 8 dims per lane; rotary partners are exchanged through LDS.
+// dq = R^T dQ~ (rotation by -theta), cast to the output type.  Row groups as
+// in the prep pass; rotary partners are exchanged through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32) {
-  __shared__ __attribute__((aligned(16))) float rowbuf[4][D];
-  const int S = p.a.S;
-  const int64_t rows = (int64_t)p.a.B * p.a.H * S;
+  using RG = RowGroups<D>;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW;
+  __shared__ __attribute__((aligned(16))) float rowbuf[4][RPW][D];
+  const int S = p.a.S, rd = p.a.rd, half = rd >> 1;
+  const int rows = p.a.B * p.a.H * S;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  if (r >= rows) return;
-  const int bh = (int)(r / S), i = (int)(r % S);
-  const int b = bh / p.a.H, h = bh % p.a.H;
-  const bool act = lane < D / 8;
-  const int d0 = 8 * lane;
-  const int rd = p.a.rd, half = rd >> 1;
-  float x[8];
+  const int g = lane & (G - 1), rw = lane / G;
+  const int wrow0 = (blockIdx.x * 4 + wave) * RPW;
+  if (wrow0 >= rows) return;  // whole waves only
+  const int r = wrow0 + rw;
+  const bool act = r < rows && g < C;
+  const int bh = r / S, i = r - bh * S;
+  const int b = bh / p.a.H, h = bh - b * p.a.H;
+  const int d0 = 8 * g;
+  const bool rot_lane = act && d0 < rd;
+  f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+  float2 cs[8];
   if (act) {
-    const float* acc = p.dq_acc + r * D + d0;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(acc);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(acc + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = lo[e];
-      x[4 + e] = hi[e];
-    }
-    if (rd > 0) {
-      *reinterpret_cast<f32x4*>(&rowbuf[wave][d0]) = lo;
-      *reinterpret_cast<f32x4*>(&rowbuf[wave][d0 + 4]) = hi;
-    }
+    const float* acc = p.dq_acc + (int64_t)r * D + d0;
+    lo = *reinterpret_cast<const f32x4*>(acc);
+    hi = *reinterpret_cast<const f32x4*>(acc + 4);
   }
-  if (rd > 0) {
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  if (!act) return;
-  if (d0 < rd) {
+  if (rot_lane) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = d0 + e;
-      if (d < rd) {
-        const bool first = d < half;
-        const float2 cs = p.a.rope[(int64_t)i * half + (first ? d : d - half)];
-        const float xp = rowbuf[wave][first ? d + half : d - half];
-        x[e] = first ? (x[e] * cs.x + xp * cs.y) : (x[e] * cs.x - xp * cs.y);
+      cs[e] = d < rd ? p.a.rope[(int64_t)i * half + (d < half ? d : d - half)]
+                     : float2{1.0f, 0.0f};
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = lo[e];
+    x[4 + e] = hi[e];
+  }
+  if (rd > 0) {
+    if (act) {
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0]) = lo;
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0 + 4]) = hi;
+    }
+    lds_wave_sync();
+    if (rot_lane) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + e;
+        if (d < rd) {
+          const bool first = d < half;
+          const float xp = rowbuf[wave][rw][first ? d + half : d - half];
+          const float sn = first ? cs[e].y : -cs[e].y;  // transpose of rotate-half
+          x[e] = fmaf(xp, sn, x[e] * cs[e].x);
+        }
       }
     }
   }
+  if (!act) return;
   if (out_f32) {
     float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
     *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
@@ -594,12 +645,16 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f
 }
 
 template <int D>
+dim3 row_grid(const BwdParams& p) {
+  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+  return dim3((unsigned)((rows + RowGroups<D>::RPB - 1) / RowGroups<D>::RPB));
+}
+
+template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
-  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-  const dim3 row_grid((unsigned)((rows + 3) / 4));
   if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
   const int nkt = (p.a.S + BNK - 1) / BNK;
@@ -610,7 +665,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
     hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(NT), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_finalize_kernel<D>), row_grid, dim3(256), 0, st, p, p.out_f32);
+  hipLaunchKernelGGL((dq_finalize_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p, p.out_f32);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev, 3, st);
 }
@@ -627,12 +682,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t*
 }
 
 hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32) {
-  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-  const dim3 grid((unsigned)((rows + 3) / 4));
   switch (p.a.D) {
-    case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), grid, dim3(256), 0, st, p, out_f32); break;
-    case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), grid, dim3(256), 0, st, p, out_f32); break;
-    case 128: hipLaunchKernelGGL((dq_finalize_kernel<128>), grid, dim3(256), 0, st, p, out_f32); break;
+    case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), row_grid<64>(p), dim3(256), 0, st, p, out_f32); break;
+    case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), row_grid<96>(p), dim3(256), 0, st, p, out_f32); break;
+    case 128: hipLaunchKernelGGL((dq_finalize_kernel<128>), row_grid<128>(p), dim3(256), 0, st, p, out_f32); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
