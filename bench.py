@@ -70,20 +70,22 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     B, H, S, D = q.shape
     ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                      device="cuda")
+    fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                      device="cuda")
     docs = None if inp.doc_offsets is None else torch.from_numpy(inp.doc_offsets).cuda()
     pos = neox.NEOX_POS_ALIBI if wl.alibi else neox.NEOX_POS_ROPE
     kw = dict(pos=pos, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
               softmax_scale=wl.softmax_scale, doc_offsets=docs)
 
     def step(ev):
-        neox.neox_attn_fwd_ex(q, k, v, o, lse, phase_events=ev[0:2], **kw)
+        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=fws, phase_events=ev[0:3], **kw)
         neox.neox_attn_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, workspace=ws,
-                              phase_events=ev[2:6], **kw)
+                              phase_events=ev[3:7], **kw)
 
-    warm_ev = make_events(torch, 6)
+    warm_ev = make_events(torch, 7)
     for _ in range(args.warmup):
         step(warm_ev)
-    events = [make_events(torch, 6) for _ in range(args.steps)]
+    events = [make_events(torch, 7) for _ in range(args.steps)]
     start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
@@ -96,8 +98,8 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     def avg(i, j):
         return sum(ev[i].elapsed_time(ev[j]) for ev in events) / len(events)
 
-    kernels_ms = {"fwd": avg(0, 1), "bwd_pre": avg(2, 3), "bwd_main": avg(3, 4),
-                  "bwd_dq_finalize": avg(4, 5)}
+    kernels_ms = {"fwd_rope_qk": avg(0, 1), "fwd": avg(1, 2), "bwd_pre": avg(3, 4),
+                  "bwd_main": avg(4, 5), "bwd_dq_finalize": avg(5, 6)}
     return total_ms, kernels_ms
 
 
@@ -108,24 +110,34 @@ def fwd_target(args, torch, np, neox, W):
     q, k, v = (dev_tensor(torch, np, getattr(inp, n), wl.dtype) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    call = lambda: neox.neox_rope_attn_fwd(q, k, v, o, lse, wl.rotary_dim, wl.rope_base,  # noqa
-                                           True, wl.softmax_scale)
-    for _ in range(args.warmup):
-        call()
-    start, end = make_events(torch, 2)
+    B, H, S, D = q.shape
+    fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                      device="cuda")
     n = max(args.steps, 20)
+    events = [make_events(torch, 3) for _ in range(n)]
+    call = lambda ev: neox.neox_attn_fwd_ex(q, k, v, o, lse, rotary_dim=wl.rotary_dim,  # noqa
+                                            rope_base=wl.rope_base, causal=True,
+                                            softmax_scale=wl.softmax_scale, workspace=fws,
+                                            phase_events=ev)
+    for _ in range(args.warmup):
+        call(events[0])
+    start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(n):
-        call()
+    for i in range(n):
+        call(events[i])
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / n
+    ms_attn = sum(ev[1].elapsed_time(ev[2]) for ev in events) / n
     flops = 4 * wl.D * W.total_pairs(inp)
     tf = flops / (ms * 1e-3) / 1e12
+    tf_attn = flops / (ms_attn * 1e-3) / 1e12
     return {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "D": wl.D,
             "rotary_dim": wl.rotary_dim, "us_per_call": round(ms * 1e3, 2),
-            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "attn_kernel_us": round(ms_attn * 1e3, 2),
+            "attn_kernel_frac": round(tf_attn / PEAK_BF16_TFLOPS, 4)}
 
 
 def cpu_baseline(args, np, W, wl, inp):
@@ -202,6 +214,10 @@ def main():
     kern = {
         "fwd": dict(flops=fwd_flops, ms=kms["fwd"], bound="mfma"),
         "bwd_main": dict(flops=bwd_flops, ms=kms["bwd_main"], bound="mfma"),
+        # q/k rotation pass of the forward: reads q and k, writes the rotated bf16 copies
+        "fwd_rope_qk": dict(bytes=2 * rows * wl.D * (el + 2)
+                            if wl.rotary_dim > 0 and el == 2 else 0,
+                            ms=kms["fwd_rope_qk"], bound="hbm"),
         # preprocess: reads o, dO and lse, writes Delta, the row log-sum-exp term and
         # the zeroed fp32 dq accumulator; with rotary it also reads q, k and writes
         # the rotated copies (bf16)
@@ -212,6 +228,8 @@ def main():
         "bwd_dq_finalize": dict(bytes=rows * wl.D * (4 + el), ms=kms["bwd_dq_finalize"],
                                 bound="hbm"),
     }
+    kern = {n: kd for n, kd in kern.items()
+            if kd["ms"] > 0 and (kd["bound"] == "mfma" or kd["bytes"] > 0)}  # passes that ran
     kernels_out = {}
     for name, kd in kern.items():
         sec = kd["ms"] * 1e-3

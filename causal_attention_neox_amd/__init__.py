@@ -23,7 +23,8 @@ from ._lib import (NEOX_BF16, NEOX_F32, NEOX_OUT_F32, NEOX_OUT_SAME, NEOX_POS_AL
 
 __all__ = [
     "NeoxError", "neox_status_str", "neox_rope_attn_fwd", "neox_rope_attn_bwd",
-    "neox_rope_attn_bwd_workspace_size", "neox_attn_fwd_ex", "neox_attn_bwd_ex",
+    "neox_rope_attn_fwd_workspace_size", "neox_rope_attn_bwd_workspace_size",
+    "neox_attn_fwd_ex", "neox_attn_bwd_ex",
     "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
     "NEOX_F32", "NEOX_BF16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
@@ -73,15 +74,26 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def neox_rope_attn_fwd_workspace_size(B: int, H: int, S: int, D: int) -> int:
+    return int(_lib.load().neox_rope_attn_fwd_workspace_size(B, H, S, D))
+
+
 def neox_rope_attn_fwd(q, k, v, o, lse, rotary_dim: int, rope_base: float = 10000.0,
                        causal: bool = True, softmax_scale: Optional[float] = None,
-                       stream=None) -> None:
-    """Calls neox_rope_attn_fwd on contiguous [B, H, S, D] tensors (o, lse written)."""
+                       workspace=None, stream=None) -> None:
+    """Calls neox_rope_attn_fwd on contiguous [B, H, S, D] tensors (o, lse written).
+    ``workspace`` is None or a uint8 device tensor of at least
+    neox_rope_attn_fwd_workspace_size() bytes (pre-rotated queries and keys)."""
     B, H, S, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = _lib.load().neox_rope_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, int(rotary_dim),
-        float(rope_base), int(bool(causal)), scale, _dtype_code(q), _stream(stream))
+        float(rope_base), int(bool(causal)), scale, _dtype_code(q), _ptr(workspace),
+        _nbytes(workspace), _stream(stream))
     _check(st, "neox_rope_attn_fwd")
 
 
@@ -97,7 +109,7 @@ def neox_rope_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, rotary_dim: int,
     ``workspace`` is a uint8 device tensor of at least the queried size."""
     B, H, S, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _nbytes(workspace)
     st = _lib.load().neox_rope_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
         B, H, S, D, int(rotary_dim), float(rope_base), int(bool(causal)), scale, _dtype_code(q),
@@ -148,17 +160,20 @@ def _make_args(q, *, pos, rotary_dim, rope_base, alibi_slopes, causal, softmax_s
 def neox_attn_fwd_ex(q, k, v, o, lse, *, pos: int = NEOX_POS_ROPE, rotary_dim: int = 0,
                      rope_base: float = 10000.0, alibi_slopes=None, causal: bool = True,
                      softmax_scale: Optional[float] = None, doc_offsets=None,
-                     out_f32: bool = False, phase_events=None, stream=None) -> None:
+                     out_f32: bool = False, workspace=None, phase_events=None,
+                     stream=None) -> None:
     """Calls neox_attn_fwd_ex; strides are taken from the tensors.
-    ``doc_offsets`` is an int32 device tensor [B, n_docs + 1]; ``phase_events``
-    is None or 2 events recorded before and after the kernel."""
+    ``doc_offsets`` is an int32 device tensor [B, n_docs + 1]; ``workspace`` as
+    for neox_rope_attn_fwd; ``phase_events`` is None or 3 events (before the
+    call, after the q/k rotation pass, after the attention kernel)."""
     a, keep = _make_args(q, pos=pos, rotary_dim=rotary_dim, rope_base=rope_base,
                          alibi_slopes=alibi_slopes, causal=causal, softmax_scale=softmax_scale,
                          doc_offsets=doc_offsets, out_f32=out_f32,
                          tensors=[q, k, v, o, None, None, None, None],
                          phase_events=phase_events)
     st = _lib.load().neox_attn_fwd_ex(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                      _ptr(lse), _stream(stream))
+                                      _ptr(lse), _ptr(workspace), _nbytes(workspace),
+                                      _stream(stream))
     del keep
     _check(st, "neox_attn_fwd_ex")
 
@@ -175,7 +190,7 @@ def neox_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, *, pos: int = NEOX_POS_R
                          alibi_slopes=alibi_slopes, causal=causal, softmax_scale=softmax_scale,
                          doc_offsets=doc_offsets, out_f32=out_f32,
                          tensors=[q, k, v, o, dout, dq, dk, dv], phase_events=phase_events)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _nbytes(workspace)
     st = _lib.load().neox_attn_bwd_ex(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                       _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                       _ptr(workspace), nbytes, _stream(stream))

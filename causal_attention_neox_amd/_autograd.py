@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import (NEOX_POS_ALIBI, NEOX_POS_ROPE, neox_attn_bwd_ex, neox_attn_fwd_ex,
-               neox_rope_attn_bwd_workspace_size)
+               neox_rope_attn_bwd_workspace_size, neox_rope_attn_fwd_workspace_size)
 
 
 class NeoxAttentionFn(torch.autograd.Function):
@@ -22,7 +22,11 @@ class NeoxAttentionFn(torch.autograd.Function):
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
         kw = dict(pos=pos, rotary_dim=rotary_dim, rope_base=rope_base, alibi_slopes=alibi_slopes,
                   causal=causal, softmax_scale=softmax_scale, doc_offsets=doc_offsets)
-        neox_attn_fwd_ex(q, k, v, o, lse, out_f32=out_f32, **kw)
+        ws = None
+        if rotary_dim > 0 and not alibi and q.dtype == torch.bfloat16:
+            ws = torch.empty(neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                             device=q.device)
+        neox_attn_fwd_ex(q, k, v, o, lse, out_f32=out_f32, workspace=ws, **kw)
         ctx.kw = kw
         ctx.out_f32 = out_f32
         ctx.save_for_backward(q, k, v, o, lse)

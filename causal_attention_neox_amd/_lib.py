@@ -50,16 +50,17 @@ class NeoxAttnArgs(ctypes.Structure):
 
 SIGNATURES = {
     "neox_status_str": (ctypes.c_char_p, [c_int]),
+    "neox_rope_attn_fwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "neox_rope_attn_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_float,
-                                   c_int, c_void_p]),
+                                   c_int, c_void_p, c_size_t, c_void_p]),
     "neox_rope_attn_bwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "neox_rope_attn_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p,
                                    c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_float,
                                    c_int, c_void_p, c_size_t, c_void_p]),
     "neox_attn_fwd_ex": (c_int, [ctypes.POINTER(NeoxAttnArgs), c_void_p, c_void_p, c_void_p,
-                                 c_void_p, c_void_p, c_void_p]),
+                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "neox_attn_bwd_ex": (c_int, [ctypes.POINTER(NeoxAttnArgs), c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),

@@ -71,27 +71,6 @@ __device__ __forceinline__ int tpos(int row, int chunk) {
 
 // ------------------------------------------------------------------------ prep
 
-// The per-row passes (prep, finalize) give each row a group of G lanes, G =
-// D/8 rounded up to a power of two, 16 B per lane, so one wave covers 64/G
-// rows and every memory instruction is full width.  Each lane issues all of
-// its loads before it uses any, and rotary partners (dims +- rd/2, which need
-// not fall on 8-dim chunk boundaries) are exchanged through LDS behind an
-// LDS-only wait, so outstanding stores never stall the exchange.
-template <int D>
-struct RowGroups {
-  static constexpr int C = D / 8;
-  static constexpr int G = C <= 8 ? 8 : 16;
-  static constexpr int RPW = 64 / G;  // rows per wave
-  static constexpr int RPB = 4 * RPW; // rows per 256-thread workgroup
-};
-
-// Waits for this wave's LDS operations only (lgkmcnt(0); vmcnt and expcnt
-// left at their maxima in the gfx9 s_waitcnt encoding).
-__device__ __forceinline__ void lds_wave_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_wave_barrier();
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   using RG = RowGroups<D>;

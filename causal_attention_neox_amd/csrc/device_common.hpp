@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, bf16
-// conversion, MFMA wrappers, document bounds, and the tile loaders that apply
-// the NeoX rotary rotation while staging rows into LDS.
+// conversion, MFMA wrappers, document bounds, the element-wise NeoX rotation
+// and the lane layout of the per-row passes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,125 +77,50 @@ __device__ __forceinline__ float alibi_slope_log2(const AttnShape& a, int h) {
 
 // Rotation of 8 consecutive dims d0..d0+7 of one row (position pos), reading
 // each partner element (d +- rd/2) from global memory.  Works for any even rd.
+// Every partner and table load is issued (at a valid address: the element
+// itself and pair 0 outside the rotary dims) before any is used, with no
+// branch in between, so the loads overlap instead of waiting one by one.
+// Requires rd > 0 (rope non-null).
 __device__ __forceinline__ void rotate8_scalar(const uint16_t* row, int d0, float* x, int pos,
                                                int rd, const float2* rope) {
   const int half = rd >> 1;
+  float xp[8];
+  float2 cs[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int d = d0 + e;
-    if (d < rd) {
-      const bool first = d < half;
-      const int p = first ? d : d - half;
-      const float xp = bf2f(row[first ? d + half : d - half]);
-      const float2 cs = rope[(int64_t)pos * half + p];
-      x[e] = first ? (x[e] * cs.x - xp * cs.y) : (x[e] * cs.x + xp * cs.y);
-    }
+    const bool in = d < rd, first = d < half;
+    xp[e] = bf2f(row[in ? (first ? d + half : d - half) : d]);
+    cs[e] = rope[(int64_t)pos * half + (in ? (first ? d : d - half) : 0)];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = d0 + e;
+    const float sn = d < half ? -cs[e].y : cs[e].y;
+    if (d < rd) x[e] = fmaf(xp[e], sn, x[e] * cs[e].x);
   }
 }
 
-// Column of tile row `r` (a multiple of 4) in a transposed LDS tile.  With
-// PERM, rows are reordered inside each group of 16 as [0-3][8-11][4-7][12-15]
-// so that an MFMA accumulator column (rows (r/4)*8 + 4*half + r%4) can feed
-// the next MFMA's B operand (8 consecutive k per lane) without a shuffle.
-template <bool PERM>
-__device__ __forceinline__ int tcol(int r) {
-  if (!PERM) return r;
-  const int g = (r >> 2) & 3;
-  const int pg = (g == 1) ? 2 : (g == 2 ? 1 : g);
-  return (r & ~15) + 4 * pg;
-}
+// Per-row passes (q/k rotation, backward prep and finalize) give each row a
+// group of G lanes, G = D/8 rounded up to a power of two, 16 B per lane, so
+// one wave covers 64/G rows and every memory instruction is full width.  Each
+// lane issues all of its loads before it uses any, and rotary partners (dims
+// +- rd/2, which need not fall on 8-dim chunk boundaries) are exchanged
+// through LDS behind an LDS-only wait, so outstanding stores never stall the
+// exchange.
+template <int D>
+struct RowGroups {
+  static constexpr int C = D / 8;
+  static constexpr int G = C <= 8 ? 8 : 16;
+  static constexpr int RPW = 64 / G;  // rows per wave
+  static constexpr int RPB = 4 * RPW; // rows per 256-thread workgroup
+};
 
-// Stages rows [r0, r0 + R) of one head's [S, D] bf16 matrix (row stride ss
-// elements) into LDS.  With ROT == 1 (rd % 8 == 0) or ROT == 2 (any even rd)
-// the first rd dims are rotated by the rotary angle of each row's position;
-// ROT == 0 copies.  Rows at or beyond S are stored as zeros.  ROWMAJOR writes
-// dst_row[row * RS + dim]; TRANS writes dst_t[dim * TS + tcol<PERM>(row)].
-// Work items are (group of 4 rows, slot of 8 dims); for ROT == 1 the first
-// rd/8 slots are "pair slots" holding dims p0..p0+3 and half+p0..half+p0+3.
-template <int D, int ROT, int R, int NT, bool ROWMAJOR, bool TRANS, bool PERM>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ base, int64_t ss, int r0,
-                                          int S, int rd, const float2* __restrict__ rope,
-                                          uint16_t* dst_row, int RS, uint16_t* dst_t, int TS,
-                                          int tid) {
-  constexpr int NSLOT = D / 8;
-  constexpr int NITEM = (R / 4) * NSLOT;
-  const int half = rd >> 1;
-  const int npair = (ROT == 1) ? (rd >> 3) : 0;
-#pragma unroll
-  for (int it0 = 0; it0 < NITEM; it0 += NT) {
-    const int it = it0 + tid;
-    if (NITEM % NT != 0 && it >= NITEM) break;
-    const int slot = it % NSLOT;
-    const int g = it / NSLOT;
-    const bool pair = slot < npair;
-    const int p0 = slot * 4;  // pair slot: first-half dims p0..p0+3
-    const int d0 = slot * 8;  // plain slot: dims d0..d0+7
-    float x[4][8];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = r0 + 4 * g + rr;
-      if (row < S) {
-        const uint16_t* src = base + (int64_t)row * ss;
-        if (pair) {
-          const u32x2 a = *reinterpret_cast<const u32x2*>(src + p0);
-          const u32x2 b = *reinterpret_cast<const u32x2*>(src + half + p0);
-          const float x1[4] = {bf_lo(a[0]), bf_hi(a[0]), bf_lo(a[1]), bf_hi(a[1])};
-          const float x2[4] = {bf_lo(b[0]), bf_hi(b[0]), bf_lo(b[1]), bf_hi(b[1])};
-          const f32x4* cs4 = reinterpret_cast<const f32x4*>(rope + (int64_t)row * half + p0);
-          const f32x4 c01 = cs4[0], c23 = cs4[1];
-          const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
-          const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[rr][e] = x1[e] * cs[e] - x2[e] * sn[e];
-            x[rr][4 + e] = x2[e] * cs[e] + x1[e] * sn[e];
-          }
-        } else {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(src + d0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[rr][2 * e] = bf_lo(w[e]);
-            x[rr][2 * e + 1] = bf_hi(w[e]);
-          }
-          if (ROT == 2) rotate8_scalar(src, d0, x[rr], row, rd, rope);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[rr][e] = 0.0f;
-      }
-    }
-    if (ROWMAJOR) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        uint16_t* dst = dst_row + (4 * g + rr) * RS;
-        if (pair) {
-          u32x2 lo, hi;
-          lo[0] = pack2(x[rr][0], x[rr][1]);
-          lo[1] = pack2(x[rr][2], x[rr][3]);
-          hi[0] = pack2(x[rr][4], x[rr][5]);
-          hi[1] = pack2(x[rr][6], x[rr][7]);
-          *reinterpret_cast<u32x2*>(dst + p0) = lo;
-          *reinterpret_cast<u32x2*>(dst + half + p0) = hi;
-        } else {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack2(x[rr][2 * e], x[rr][2 * e + 1]);
-          *reinterpret_cast<u32x4*>(dst + d0) = w;
-        }
-      }
-    }
-    if (TRANS) {
-      const int col = tcol<PERM>(4 * g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = pair ? (e < 4 ? p0 + e : half + p0 + e - 4) : d0 + e;
-        u32x2 w;
-        w[0] = pack2(x[0][e], x[1][e]);
-        w[1] = pack2(x[2][e], x[3][e]);
-        *reinterpret_cast<u32x2*>(dst_t + dim * TS + col) = w;
-      }
-    }
-  }
+// Waits for this wave's LDS operations only (lgkmcnt(0); vmcnt and expcnt
+// left at their maxima in the gfx9 s_waitcnt encoding).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace neox

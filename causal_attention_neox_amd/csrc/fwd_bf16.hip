@@ -26,6 +26,10 @@
 //    exp2 domain), so O and the row sum are rescaled rarely.
 //  * Workgroups are issued heaviest q-tile first, heads fastest: with B*H a
 //    multiple of 8 all q-tiles of a head share one XCD and its L2.
+//  * With a caller workspace, a row pass first writes q~ = R q and k~ = R k
+//    (the NeoX pipeline rotates q and k before attention), and the attention
+//    kernel runs its rotation-free form on them.  Without one, Q~ is rotated
+//    when a workgroup loads it and the rotary K dims at every tile visit.
 #include "device_common.hpp"
 
 namespace neox {
@@ -355,7 +359,9 @@ struct FwdState {
   }
 };
 
-template <int D, int ROT, bool ALIBI>
+// ROT: how K tiles are staged (0: plain or pre-rotated K; 1, 2: rotary pair
+// items; 3: every chunk through registers).  QROT: rotate Q~ at load.
+template <int D, int ROT, bool ALIBI, bool QROT>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int CPR = D / 8;
   constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
         x[2 * e] = bf_lo(w[e]);
         x[2 * e + 1] = bf_hi(w[e]);
       }
-      if (ROT != 0) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
+      if (QROT) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
       if (qi >= S) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -493,36 +499,134 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int ROT, bool ALIBI>
+// q~ = R q and k~ = R k for every row, into contiguous bf16 [B][H][S][D]
+// buffers (one pass: both use the row's own position).  Each wave handles NR
+// row groups with every load issued before the first use.
+template <int D>
+__global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
+  using RG = RowGroups<D>;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW, NR = 2;
+  __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][NR][RPW][2][D];
+  const AttnShape& a = p.a;
+  const int S = a.S, rd = a.rd, half = rd >> 1;
+  const int rows = a.B * a.H * S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane & (G - 1), rw = lane / G;
+  const int wrow0 = (blockIdx.x * 4 + wave) * RPW * NR;
+  if (wrow0 >= rows) return;  // whole waves only
+  const int d0 = 8 * g;
+  int r[NR], pos[NR];
+  bool act[NR];
+  u32x4 w[NR][2];
+  float2 cs[NR][8];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    r[n] = wrow0 + n * RPW + rw;
+    act[n] = r[n] < rows && g < C;
+    const int bh = r[n] / S, i = r[n] - bh * S;
+    const int b = bh / a.H, h = bh - b * a.H;
+    pos[n] = i;
+    w[n][0] = w[n][1] = u32x4{0u, 0u, 0u, 0u};
+    if (act[n]) {
+      w[n][0] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
+                                                (int64_t)i * p.sq.s + d0);
+      w[n][1] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
+                                                (int64_t)i * p.sk.s + d0);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    if (act[n] && d0 < rd) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + e;
+        cs[n][e] = d < rd ? a.rope[(int64_t)pos[n] * half + (d < half ? d : d - half)]
+                          : float2{1.0f, 0.0f};
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NR; ++n)
+    if (act[n]) {
+      *reinterpret_cast<u32x4*>(&rowbuf[wave][n][rw][0][d0]) = w[n][0];
+      *reinterpret_cast<u32x4*>(&rowbuf[wave][n][rw][1][d0]) = w[n][1];
+    }
+  lds_wave_sync();
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    if (!act[n]) continue;
+    if (d0 < rd) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf_lo(w[n][t][e]);
+          x[2 * e + 1] = bf_hi(w[n][t][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = d0 + e;
+          if (d < rd) {
+            const bool first = d < half;
+            const float sn = first ? -cs[n][e].y : cs[n][e].y;  // rotate-half: (-x2, x1)
+            x[e] = fmaf(bf2f(rowbuf[wave][n][rw][t][first ? d + half : d - half]), sn,
+                        x[e] * cs[n][e].x);
+          }
+        }
+        w[n][t] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+      }
+    }
+    *reinterpret_cast<u32x4*>(p.qrot + (int64_t)r[n] * D + d0) = w[n][0];
+    *reinterpret_cast<u32x4*>(p.krot + (int64_t)r[n] * D + d0) = w[n][1];
+  }
+}
+
+template <int D, int ROT, bool ALIBI, bool QROT>
 hipError_t launch_d(const FwdParams& p, hipStream_t st) {
   const int nqt = (p.a.S + BM - 1) / BM;
   const dim3 grid((unsigned)(nqt * p.a.B * p.a.H));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROT, ALIBI>), grid, dim3(NT), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROT, ALIBI, QROT>), grid, dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
-template <int D, bool ALIBI>
-hipError_t launch_rot(const FwdParams& p, hipStream_t st) {
-  const int rd = p.a.rd;
-  if (rd == 0) return launch_d<D, 0, ALIBI>(p, st);
-  if (rd % 16 == 0) return launch_d<D, 1, ALIBI>(p, st);
-  if (rd % 8 == 0) return launch_d<D, 2, ALIBI>(p, st);
-  return launch_d<D, 3, ALIBI>(p, st);
-}
-
 template <int D>
-hipError_t launch_alibi(const FwdParams& p, hipStream_t st) {
-  if (p.a.alibi) return launch_d<D, 0, true>(p, st);  // ALiBi runs without rotary
-  return launch_rot<D, false>(p, st);
+hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+  hipError_t e;
+  const int rd = p.a.rd;
+  if (p.a.alibi) {  // ALiBi runs without rotary
+    if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
+    return launch_d<D, 0, true, false>(p, st);
+  }
+  if (rd > 0 && p.qrot) {
+    const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+    const int rows_per_block = 2 * RowGroups<D>::RPB;
+    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+    hipLaunchKernelGGL((rope_qk_kernel<D>), grid, dim3(256), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
+    FwdParams q = p;
+    const Strides dense{(int64_t)p.a.H * p.a.S * D, (int64_t)p.a.S * D, D};
+    q.q = p.qrot;
+    q.sq = dense;
+    q.k = p.krot;
+    q.sk = dense;
+    return launch_d<D, 0, false, false>(q, st);
+  }
+  if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
+  if (rd == 0) return launch_d<D, 0, false, false>(p, st);
+  if (rd % 16 == 0) return launch_d<D, 1, false, true>(p, st);
+  if (rd % 8 == 0) return launch_d<D, 2, false, true>(p, st);
+  return launch_d<D, 3, false, true>(p, st);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st) {
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   switch (p.a.D) {
-    case 64: return launch_alibi<64>(p, st);
-    case 96: return launch_alibi<96>(p, st);
-    case 128: return launch_alibi<128>(p, st);
+    case 64: return launch_dim<64>(p, st, ev);
+    case 96: return launch_dim<96>(p, st, ev);
+    case 128: return launch_dim<128>(p, st, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,7 +34,9 @@ struct FwdParams {
   void* o;
   float* lse;
   Strides sq, sk, sv, so;
-  int out_f32;  // o stored as fp32
+  int out_f32;     // o stored as fp32
+  uint16_t* qrot;  // bf16 [B][H][S][D] workspace parts for q~ = R q and k~ = R k,
+  uint16_t* krot;  // or null (bf16 path; rotation then happens in the kernel)
 };
 
 struct BwdParams {
@@ -59,7 +61,10 @@ struct BwdParams {
 
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
 
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st);
+// `ev` is null or 3 events: [0] is recorded by the caller before the call;
+// the launcher records [1] after the q/k rotation pass (before the attention
+// kernel when there is none); the caller records [2] after the call.
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
 
 // `ev` is null or 4 events recorded before the preprocess kernel, after it,

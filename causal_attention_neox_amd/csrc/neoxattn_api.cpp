@@ -203,6 +203,13 @@ size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D) {
   return bwd_workspace_layout(B, H, S, D, &w) ? w.total : 0;
 }
 
+size_t neox_rope_attn_fwd_workspace_size(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1 || D < 1 || D > 4096) return 0;
+  const int64_t rows = (int64_t)B * H * S;
+  if (rows >= kMaxRows) return 0;
+  return 2 * round256((size_t)rows * (size_t)D * 2u);
+}
+
 const char* neox_status_str(int status) {
   switch (status) {
     case NEOX_OK: return "ok";
@@ -218,7 +225,8 @@ const char* neox_status_str(int status) {
 }
 
 int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, const void* v,
-                     void* o, float* lse, void* stream) {
+                     void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   int st = validate_common(a);
   if (st != NEOX_OK) return st;
   const neox_strides def = contiguous(a);
@@ -231,6 +239,11 @@ int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   if ((st = check_tensor(o, s ? s[3] : def, unit_out)) != NEOX_OK) return st;
   if (!lse) return NEOX_E_ARG;
   if (!aligned16(lse)) return NEOX_E_ALIGN;
+  if (workspace) {
+    if (workspace_bytes < neox_rope_attn_fwd_workspace_size(a->B, a->H, a->S, a->D))
+      return NEOX_E_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NEOX_E_ALIGN;
+  }
 
   int dev = 0;
   if ((st = check_device(&dev)) != NEOX_OK) return st;
@@ -250,12 +263,22 @@ int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   p.sv = to_internal(s ? s[2] : def);
   p.so = to_internal(s ? s[3] : def);
   p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
+  p.qrot = reinterpret_cast<uint16_t*>(workspace);
+  p.krot = workspace ? reinterpret_cast<uint16_t*>(
+                           reinterpret_cast<char*>(workspace) +
+                           round256((size_t)a->B * a->H * a->S * (size_t)a->D * 2u))
+                     : nullptr;
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
   if (neox::record_event(ev, 0, hs) != hipSuccess) return NEOX_E_LAUNCH;
-  const hipError_t e = a->dtype == NEOX_BF16 ? neox::launch_fwd_bf16(p, hs)
-                                             : neox::launch_fwd_f32(p, hs);
+  hipError_t e;
+  if (a->dtype == NEOX_BF16) {
+    e = neox::launch_fwd_bf16(p, hs, ev);
+  } else {
+    e = neox::record_event(ev, 1, hs);
+    if (e == hipSuccess) e = neox::launch_fwd_f32(p, hs);
+  }
   if (e != hipSuccess) return NEOX_E_LAUNCH;
-  return neox::record_event(ev, 1, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
+  return neox::record_event(ev, 2, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
 }
 
 int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, const void* v,
@@ -324,7 +347,8 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
 
 int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int S, int D, int rotary_dim, float rope_base, int causal,
-                       float softmax_scale, int dtype, void* stream) {
+                       float softmax_scale, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   neox_attn_args a;
   std::memset(&a, 0, sizeof(a));
   a.B = B;
@@ -338,7 +362,7 @@ int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   a.causal = causal;
   a.softmax_scale = softmax_scale;
   a.out_dtype = NEOX_OUT_SAME;
-  return neox_attn_fwd_ex(&a, q, k, v, o, lse, stream);
+  return neox_attn_fwd_ex(&a, q, k, v, o, lse, workspace, workspace_bytes, stream);
 }
 
 int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -107,10 +107,12 @@ typedef struct neox_strides {
  *                q, k, v, o, dout, dq, dk, dv (the fwd reads the first 4).
  *  phase_events  NULL, or hipEvent_t handles (as void*) that the call records
  *                on `stream` around its kernels, for timing by the caller: the
- *                forward records [0] before and [1] after its kernel; the
- *                backward records [0] before the preprocess kernel, [1] after
- *                it, [2] after the main kernel(s) and [3] after the dq
- *                finalize.  The events are owned by the caller.
+ *                forward records [0] before its first kernel, [1] after the q/k
+ *                rotation pass (right after [0] when none runs) and [2] after
+ *                the attention kernel; the backward records [0] before the
+ *                preprocess kernel, [1] after it, [2] after the main kernel(s)
+ *                and [3] after the dq finalize.  The events are owned by the
+ *                caller.
  */
 typedef struct neox_attn_args {
   int B, H, S, D;
@@ -132,14 +134,32 @@ typedef struct neox_attn_args {
 const char* neox_status_str(int status);
 
 /*
- * Forward.  q, k, v: [B, H, S, D] of `dtype` (read only).  o: [B, H, S, D] of
- * `dtype` (written).  lse: [B, H, S] fp32 natural-log logsumexp of each row's
- * allowed scores (written; the backward needs it).  rotary_dim = 0 turns the
- * rotation off.  Causal masking when causal != 0.
+ * Bytes of the optional forward workspace: two bf16 [B, H, S, D] buffers that
+ * receive the rotated rows q~ = R q and k~ = R k (NeoX rotate-half with each
+ * row's own position; "FasterTransformer GPT-NeoX 推理指南", section
+ * "模型配置": both Q and K are rotated), written by one row pass so that the
+ * attention kernel itself does no rotation.  2 * (B*H*S*D*2 rounded up to
+ * 256) bytes.  Returns 0 for sizes that are invalid (<= 0) or overflow.
+ */
+size_t neox_rope_attn_fwd_workspace_size(int B, int H, int S, int D);
+
+/*
+ * Forward of causal self-attention with NeoX rotary embedding, in the tiled
+ * exact form with an online softmax ("GPT-NeoX 开源训练框架深度解读",
+ * section on attention speed: FlashAttention).  q, k, v: [B, H, S, D] of
+ * `dtype` (read only).  o: [B, H, S, D] of `dtype` (written).  lse: [B, H, S]
+ * fp32 natural-log logsumexp of each row's allowed scores (written; the
+ * backward needs it).  rotary_dim = 0 turns the rotation off.  Causal masking
+ * when causal != 0.  workspace: NULL, or caller-owned device memory of at
+ * least neox_rope_attn_fwd_workspace_size() bytes, 256-byte aligned,
+ * overwritten by the call; it is used by the bf16 path with rotary_dim > 0
+ * (the faster path) and ignored otherwise.  Results do not depend on whether
+ * a workspace is given beyond fp32 rounding order of the rotation.
  */
 int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int S, int D, int rotary_dim, float rope_base,
-                       int causal, float softmax_scale, int dtype, void* stream);
+                       int causal, float softmax_scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace the backward needs, in five 256-byte aligned
  * parts: an fp32 [B, H, S, D] dq accumulator, two fp32 [B, H, S] row terms
@@ -164,9 +184,11 @@ int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int causal, float softmax_scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Forward with ALiBi, packed documents, strides and output type (see neox_attn_args). */
+/* Forward with ALiBi, packed documents, strides and output type (see
+ * neox_attn_args); workspace as for neox_rope_attn_fwd. */
 int neox_attn_fwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,
-                     void* o, float* lse, void* stream);
+                     void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* Backward counterpart of neox_attn_fwd_ex; workspace as for neox_rope_attn_bwd. */
 int neox_attn_bwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,

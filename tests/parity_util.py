@@ -31,8 +31,10 @@ def to_f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force_ex: bool = False):
-    """Forward (and backward) on the GPU through the C ABI; returns torch tensors."""
+def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force_ex: bool = False,
+                fwd_workspace: bool = True):
+    """Forward (and backward) on the GPU through the C ABI; returns torch tensors.
+    ``fwd_workspace`` gives the forward its optional workspace (pre-rotated queries and keys)."""
     torch = torch_mod()
     wl = inp.wl
     q, k, v = (to_device(inp, n) for n in ("q", "k", "v"))
@@ -44,17 +46,21 @@ def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force
     pos = neox.NEOX_POS_ALIBI if wl.alibi else neox.NEOX_POS_ROPE
     kw = dict(pos=pos, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
               softmax_scale=wl.softmax_scale, doc_offsets=docs, out_f32=out_f32)
+    B, H, S, D = q.shape
+    fws = None
+    if fwd_workspace:
+        fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                          device="cuda")
     if use_ex:
-        neox.neox_attn_fwd_ex(q, k, v, o, lse, **kw)
+        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=fws, **kw)
     else:
         neox.neox_rope_attn_fwd(q, k, v, o, lse, wl.rotary_dim, wl.rope_base, wl.causal,
-                                wl.softmax_scale)
+                                wl.softmax_scale, workspace=fws)
     res = {"o": o, "lse": lse}
     if backward:
         do = to_device(inp, "dout")
         o_in = o if o.dtype == q.dtype else o.to(q.dtype)
         dq, dk, dv = (torch.empty(q.shape, dtype=odt, device="cuda") for _ in range(3))
-        B, H, S, D = q.shape
         ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                          device="cuda")
         if use_ex:

@@ -44,7 +44,8 @@ def declared_functions():
 def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ("neox_rope_attn_fwd", "neox_rope_attn_bwd", "neox_rope_attn_bwd_workspace_size",
-              "neox_attn_fwd_ex", "neox_attn_bwd_ex", "neox_status_str"):
+              "neox_rope_attn_fwd_workspace_size", "neox_attn_fwd_ex", "neox_attn_bwd_ex",
+              "neox_status_str"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover the header"
 
@@ -67,9 +68,9 @@ def test_status_strings(lib):
 
 
 def fwd(lib, q=A1, k=A2, v=A3, o=A4, lse=A5, B=2, H=4, S=128, D=64, rd=16, base=1e4, causal=1,
-        scale=0.125, dtype=BF16):
+        scale=0.125, dtype=BF16, ws=None, wsb=0):
     return lib.neox_rope_attn_fwd(q, k, v, o, lse, B, H, S, D, rd, base, causal, scale, dtype,
-                                  None)
+                                  ws, wsb, None)
 
 
 def bwd(lib, ws=None, wsb=None, dq=A7, B=2, H=4, S=128, D=64, rd=16, dtype=BF16, **kw):
@@ -91,6 +92,21 @@ def bwd(lib, ws=None, wsb=None, dq=A7, B=2, H=4, S=128, D=64, rd=16, dtype=BF16,
 ])
 def test_forward_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def test_forward_workspace_validation(lib):
+    """The forward workspace is optional; when given it must be large enough
+    and 256-byte aligned (checked before any device work)."""
+    need = lib.neox_rope_attn_fwd_workspace_size(2, 4, 128, 64)
+    assert need == 2 * (2 * 4 * 128 * 64 * 2)  # rotated q and k, bf16
+    assert fwd(lib, ws=P(0x100000), wsb=need - 1) == E_WS
+    assert fwd(lib, ws=P(0x100010), wsb=need) == E_ALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert fwd(lib, ws=P(0x100000), wsb=need) == E_DEV
+        assert fwd(lib, ws=None, wsb=0) == E_DEV
+    assert lib.neox_rope_attn_fwd_workspace_size(0, 1, 1, 64) == 0
+    assert lib.neox_rope_attn_fwd_workspace_size(1 << 16, 1 << 8, 1 << 8, 64) == 0
+    assert lib.neox_rope_attn_fwd_workspace_size(1, 1, 3, 96) == 2 * 768  # 576 rounded up, x2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -125,7 +141,7 @@ def make_args(**kw):
 ])
 def test_ex_validation(lib, kw, status):
     a = make_args(**kw)
-    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == status
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) == status
 
 
 def test_ex_strides_validation(lib):
@@ -134,16 +150,16 @@ def test_ex_strides_validation(lib):
         strides[n] = _lib.NeoxStrides(4 * 128 * 192, 128 * 192, 192)
     a = make_args(strides=ctypes.cast(strides, ctypes.POINTER(_lib.NeoxStrides)))
     # valid strides: validation passes, so the call stops at the device check on a CPU host
-    st = lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None)
+    st = lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None)
     assert st in (OK, E_DEV)
     strides[1] = _lib.NeoxStrides(4 * 128 * 192, 128 * 192, 100)  # k rows not 16-byte aligned
-    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == E_ALIGN
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) == E_ALIGN
     strides[1] = _lib.NeoxStrides(-1, 0, 64)
-    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None) == E_ARG
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) == E_ARG
 
 
 def test_null_args_struct(lib):
-    assert lib.neox_attn_fwd_ex(None, A1, A2, A3, A4, A5, None) == E_ARG
+    assert lib.neox_attn_fwd_ex(None, A1, A2, A3, A4, A5, None, 0, None) == E_ARG
     assert lib.neox_attn_bwd_ex(None, A1, A2, A3, A4, A5, A6, A7, A8, A9, A1, 1 << 30,
                                 None) == E_ARG
 
