@@ -99,7 +99,7 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
         return sum(ev[i].elapsed_time(ev[j]) for ev in events) / len(events)
 
     kernels_ms = {"fwd_rope_qk": avg(0, 1), "fwd": avg(1, 2), "bwd_pre": avg(3, 4),
-                  "bwd_main": avg(4, 5), "bwd_dq_finalize": avg(5, 6)}
+                  "bwd_dkdv": avg(4, 5), "bwd_dq": avg(5, 6)}
     return total_ms, kernels_ms
 
 
@@ -213,20 +213,21 @@ def main():
     el = 2 if wl.dtype == "bf16" else 4
     kern = {
         "fwd": dict(flops=fwd_flops, ms=kms["fwd"], bound="mfma"),
-        "bwd_main": dict(flops=bwd_flops, ms=kms["bwd_main"], bound="mfma"),
+        # dK/dV pass: S, dP, dV, dK products (8 D flop per allowed pair)
+        "bwd_dkdv": dict(flops=8 * wl.D * pairs, ms=kms["bwd_dkdv"], bound="mfma"),
+        # dQ pass: the dQ product is its algorithmic work (2 D per pair); it also
+        # recomputes S and dP (4 D per pair, reported as "executed")
+        "bwd_dq": dict(flops=2 * wl.D * pairs, executed=6 * wl.D * pairs, ms=kms["bwd_dq"],
+                       bound="mfma"),
         # q/k rotation pass of the forward: reads q and k, writes the rotated bf16 copies
         "fwd_rope_qk": dict(bytes=2 * rows * wl.D * (el + 2)
                             if wl.rotary_dim > 0 and el == 2 else 0,
                             ms=kms["fwd_rope_qk"], bound="hbm"),
-        # preprocess: reads o, dO and lse, writes Delta, the row log-sum-exp term and
-        # the zeroed fp32 dq accumulator; with rotary it also reads q, k and writes
-        # the rotated copies (bf16)
-        "bwd_pre": dict(bytes=rows * wl.D * (2 * el + 4) + rows * 12
+        # preprocess: reads o, dO and lse, writes Delta and the row log-sum-exp term;
+        # with rotary it also reads q, k and writes the rotated bf16 copies
+        "bwd_pre": dict(bytes=2 * rows * wl.D * el + rows * 12
                         + (rows * wl.D * (2 * el + 4) if wl.rotary_dim > 0 and el == 2 else 0),
                         ms=kms["bwd_pre"], bound="hbm"),
-        # finalize: reads the fp32 dq accumulator, writes dq
-        "bwd_dq_finalize": dict(bytes=rows * wl.D * (4 + el), ms=kms["bwd_dq_finalize"],
-                                bound="hbm"),
     }
     kern = {n: kd for n, kd in kern.items()
             if kd["ms"] > 0 and (kd["bound"] == "mfma" or kd["bytes"] > 0)}  # passes that ran
@@ -237,6 +238,8 @@ def main():
             ach = kd["flops"] / sec / 1e12
             kernels_out[name] = {"us": round(kd["ms"] * 1e3, 2), "tflops": round(ach, 1),
                                  "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+            if "executed" in kd:
+                kernels_out[name]["executed_tflops"] = round(kd["executed"] / sec / 1e12, 1)
         else:
             ach = kd["bytes"] / sec / 1e9
             kernels_out[name] = {"us": round(kd["ms"] * 1e3, 2), "gbs": round(ach, 1),

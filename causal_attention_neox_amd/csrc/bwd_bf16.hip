@@ -3,42 +3,34 @@
 // Recompute-based backward of the tiled exact attention (GPT-NeoX trains with
 // the FlashAttention-2 form, "GPT-NeoX 开源训练框架深度解读", section
 // "问题二：注意力计算太慢"): probabilities are rebuilt from the forward's row
-// logsumexp instead of being stored, so memory stays O(S).
+// logsumexp instead of being stored, so memory stays O(S).  Three passes:
 //
-//   prep:     per row, Delta_i = dO_i . o_i, nlse_i = -lse_i log2(e) (with the
-//             ALiBi row term folded in), the fp32 dQ~ accumulator zeroed, and
-//             the rotated rows q~ = R q, k~ = R k written once to the workspace
-//             (NeoX rotate-half, "FasterTransformer GPT-NeoX 推理指南"), so the
-//             main loop never rotates.
-//   main:     one workgroup per (batch, head, 128 keys); K~ and V stay in
-//             registers (and K~ in LDS) while q-tiles of 64 rows stream through:
-//               S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
-//               dS = P (dP - Delta) scale,
-//               dV^T += dO^T P,   dK~^T += Q~^T dS   (registers),
-//               dQ~ += dS K~                       (fp32 atomics, coalesced).
-//             The epilogue applies R^T (rotation by -theta) to dK~ and writes
-//             dK and dV.
-//   finalize: dq = R^T dQ~, cast to the output type.
+//   prep:  per row, Delta_i = dO_i . o_i, nlse_i = -lse_i log2(e) (with the
+//          ALiBi row term folded in), and the rotated rows q~ = R q, k~ = R k
+//          written once to the workspace (NeoX rotate-half, "FasterTransformer
+//          GPT-NeoX 推理指南"), so the other passes never rotate.
+//   dK/dV: one workgroup per (batch, head, 128 keys), K-stationary; 64-row
+//          q-tiles stream through LDS:
+//            S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
+//            dS' = P (dP - Delta),  dV^T += dO^T P,  dK~^T += Q~^T dS'.
+//          The epilogue writes dV and dK = scale R^T dK~.
+//   dQ:    one workgroup per (batch, head, 128 queries), Q-stationary; 64-key
+//          tiles stream through LDS, S and dP are recomputed, dQ~ += dS' K~
+//          accumulates in registers, and the epilogue writes dq = scale R^T dQ~.
 //
-// Orientation: S and dP use M = queries, N = keys, so each lane owns one key
-// and P / dS are directly the B operands of the dV^T and dK~^T products.  The
-// transposed operands (dO^T, Q~^T, dS^T, K~^T) come from row-major LDS tiles
-// through ds_read_b64_tr_b16.  Q~ and dO tiles go global -> LDS directly
-// (global_load_lds_dwordx4), double buffered with dS, one barrier per tile.
+// Splitting dQ off costs two extra products (S and dP recomputed) but needs
+// no fp32 atomics: accumulating dQ~ across key blocks with atomics is bound by
+// the L2 atomic rate (about one 4-byte add per channel per clock), far below
+// the matrix cores, and it also makes dq deterministic.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace neox {
 namespace {
 
-constexpr int BNK = 128;  // keys per workgroup (4 waves x 32)
+constexpr int BNK = 128;  // keys per dK/dV workgroup (4 key groups x 32)
 constexpr int NT = 256;
-// Queries per streamed tile: 64, or 32 at D = 128 where the stationary
-// operands and accumulators leave less room for the score tiles.
-template <int D>
-struct QTile {
-  static constexpr int BMQ = D == 128 ? 32 : 64;
-};
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ s16x4 tr4(const uint16_t* p) {
@@ -123,9 +115,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 #pragma unroll
   for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
   if (act) {
-    float* acc = p.dq_acc + (int64_t)r * D + d0;
-    *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (g == 0) {
       p.delta[r] = sum;
       float nl = -lse * kLog2e;
@@ -169,29 +158,37 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------------ main
+// ------------------------------------------------------------------- dK / dV
 
+// Eight waves, two per SIMD.  Wave w owns the 32 keys 32 (w & 3) .. +31 of
+// the workgroup's 128 and query half w >> 2 (32 rows) of every 64-row q-tile;
+// the two waves of a key group add their dV / dK~ partial sums in the
+// epilogue.  K~ and V are the B operands of S and dP: held in registers where
+// they fit (D = 64), else re-read from stationary LDS tiles.
 template <int D>
-struct BwdLds {
-  static constexpr int BMQ = QTile<D>::BMQ;
+struct DkdvLds {
+  static constexpr int BMQ = 64;
   static constexpr int C = D / 8;
+  static constexpr bool kRegKV = D <= 64;        // K~ and V B operands held in registers
   static constexpr int KT = 0;                   // K~ [BNK][D]
-  static constexpr int Q0 = KT + BNK * D;        // Q~ tiles [BMQ][D] x2
+  static constexpr int VT = KT + BNK * D;        // V [BNK][D] (when not in registers)
+  static constexpr int Q0 = VT + (kRegKV ? 0 : BNK * D);  // Q~ tiles [BMQ][D] x2
   static constexpr int G0 = Q0 + 2 * BMQ * D;    // dO tiles x2
-  static constexpr int DS0 = G0 + 2 * BMQ * D;   // dS tiles [BNK][BMQ] x2 (rows of BMQ/8 chunks)
-  static constexpr int F0 = DS0 + 2 * BNK * BMQ; // floats: nlse x2, Delta x2 (BMQ each)
+  static constexpr int F0 = G0 + 2 * BMQ * D;    // floats: nlse x2, Delta x2 (BMQ each)
   static constexpr int N16 = F0 + 2 * 4 * BMQ;   // total in uint16 units
   static_assert((F0 * 2) % 16 == 0, "float area alignment");
 };
+constexpr int NT8 = 512;
 
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
-  using L = BwdLds<D>;
+__global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using L = DkdvLds<D>;
   constexpr int BMQ = L::BMQ;
-  constexpr int QB = BMQ / 32;   // 32-query blocks per tile
-  constexpr int CS = BMQ / 8;    // 16-byte chunks per dS row
   constexpr int C = L::C;
   constexpr int NB = D / 32;
+  constexpr int NFB = 2 * C / 8;  // 1 KB direct-load blocks per wave (per tile / stationary pair)
+  static_assert((2 * C) % 8 == 0, "tile blocks must split evenly over 8 waves");
+  constexpr bool kRegKV = L::kRegKV;
   __shared__ __attribute__((aligned(16))) uint16_t lds[L::N16];
   float* fl = reinterpret_cast<float*>(lds + L::F0);  // nlse[2][BMQ], delta[2][BMQ]
 
@@ -202,23 +199,23 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kg = wave & 3, qhalf = wave >> 2;
   const int ql = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4, j16 = lane & 15;
   const int k0 = kt * BNK;
-  const int j = k0 + 32 * wave + ql;  // this lane's key
+  const int j = k0 + 32 * kg + ql;  // this lane's key
 
   const bool rot = a.rd > 0;
   const uint16_t* qb = rot ? p.qrot + (int64_t)bh * S * D
                            : (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
-  const int64_t qs = rot ? D : p.sq.s;
+  const int64_t qstr = rot ? D : p.sq.s;
   const uint16_t* kb = rot ? p.krot + (int64_t)bh * S * D
                            : (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
-  const int64_t ks = rot ? D : p.sk.s;
+  const int64_t kstr = rot ? D : p.sk.s;
   const uint16_t* vb = (const uint16_t*)p.v + b * p.sv.b + h * p.sv.h;
   const uint16_t* gb = (const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h;
   const float* nlb = p.nlse + (int64_t)bh * S;
   const float* dlb = p.delta + (int64_t)bh * S;
-  float* dqab = p.dq_acc + (int64_t)bh * S * D;
 
   // Queries that may see this lane's key: [qlo, qhi].
   const int32_t* drow = a.docs ? a.docs + (int64_t)b * (a.n_docs + 1) : nullptr;
@@ -241,127 +238,104 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
   }
   const int qt_lo = bqlo / BMQ, qt_hi = bqhi / BMQ + 1;
 
-  // Direct-load plans: tile position P = 64 * block + lane -> (row, chunk).
-  // K~: BNK*C/64 blocks over 4 waves; Q~ and dO tiles: BMQ*C/64 = C blocks.
-  constexpr int NKB = BNK * C / 64 / 4;
-  constexpr int NQB = BMQ * C / 64 / 4;
-  int qoff[NQB], goff[NQB];
+  // Direct-load plan of a q-tile: 2C blocks of 64 chunks (C of Q~, then C of
+  // dO); this wave loads blocks wave + 8 n.  Position P = 64 * blk + lane of a
+  // tile -> (row P / C, chunk (P % C) ^ swizzle(row)).
+  int foff[NFB], fdst[NFB];
+  bool fdo[NFB];
 #pragma unroll
-  for (int n = 0; n < NQB; ++n) {
-    const int P = 64 * (wave + 4 * n) + lane;
+  for (int n = 0; n < NFB; ++n) {
+    const int fbk = wave + 8 * n;
+    fdo[n] = fbk >= C;
+    const int blk = fdo[n] ? fbk - C : fbk;
+    const int P = 64 * blk + lane;
     const int row = P / C, ch = (P % C) ^ swz<C>(row);
-    qoff[n] = (int)(row * qs) + 8 * ch;
-    goff[n] = (int)(row * p.sdo.s) + 8 * ch;
+    foff[n] = (int)(row * (fdo[n] ? p.sdo.s : qstr)) + 8 * ch;
+    fdst[n] = (fdo[n] ? L::G0 - L::Q0 : 0) + 512 * blk;
   }
-  auto fetch_q = [&](int qt, int buf) {
+  // Q~ tile to Qd, dO tile to Qd + G0 - Q0, nlse to Fd[0..BMQ), Delta to
+  // Fd[2 BMQ..); on the last tile rows past S re-read row S-1 (masked).
+  auto fetch_q = [&](int qt, uint16_t* Qd, float* Fd) {
     const int q0 = qt * BMQ;
-    uint16_t* Qt = lds + L::Q0 + buf * BMQ * D;
-    uint16_t* Gt = lds + L::G0 + buf * BMQ * D;
     if (q0 + BMQ <= S) {
-      const uint16_t* q_t = qb + (int64_t)q0 * qs;
+      const uint16_t* q_t = qb + (int64_t)q0 * qstr;
       const uint16_t* g_t = gb + (int64_t)q0 * p.sdo.s;
 #pragma unroll
-      for (int n = 0; n < NQB; ++n) {
-        load_lds16(q_t + qoff[n], Qt + 512 * (wave + 4 * n));
-        load_lds16(g_t + goff[n], Gt + 512 * (wave + 4 * n));
-      }
-      if ((S & 3) == 0) {  // rows of nlse / Delta start 16-byte aligned
-        if (wave == 0 && lane < BMQ / 4)
-          load_lds16(nlb + q0 + 4 * lane, lds + L::F0 + buf * 2 * BMQ);
-        if (wave == 1 && lane < BMQ / 4)
-          load_lds16(dlb + q0 + 4 * lane, lds + L::F0 + 4 * BMQ + buf * 2 * BMQ);
-      } else if (wave < 2 && lane < BMQ / 4) {
-        const float* src = wave == 0 ? nlb : dlb;
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = src[q0 + 4 * lane + e];
-        *reinterpret_cast<f32x4*>(fl + wave * 2 * BMQ + buf * BMQ + 4 * lane) = w;
-      }
+      for (int n = 0; n < NFB; ++n) load_lds16((fdo[n] ? g_t : q_t) + foff[n], Qd + fdst[n]);
     } else {
-      // last tile: rows past S re-read row S-1 (their P is masked to 0)
 #pragma unroll
-      for (int n = 0; n < NQB; ++n) {
-        const int P = 64 * (wave + 4 * n) + lane;
+      for (int n = 0; n < NFB; ++n) {
+        const int fbk = wave + 8 * n;
+        const int blk = fdo[n] ? fbk - C : fbk;
+        const int P = 64 * blk + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
         const int rr = min(q0 + row, S - 1);
-        load_lds16(qb + (int64_t)rr * qs + 8 * ch, Qt + 512 * (wave + 4 * n));
-        load_lds16(gb + (int64_t)rr * p.sdo.s + 8 * ch, Gt + 512 * (wave + 4 * n));
+        const uint16_t* src = fdo[n] ? gb + (int64_t)rr * p.sdo.s : qb + (int64_t)rr * qstr;
+        load_lds16(src + 8 * ch, Qd + fdst[n]);
       }
-      // nlse / Delta: 4 floats per lane; rows past S get 0 and are masked
-      if (wave < 2 && lane < BMQ / 4) {
-        const float* src = wave == 0 ? nlb : dlb;
+    }
+    if (wave < 2 && lane < BMQ / 4) {
+      const float* src = wave == 0 ? nlb : dlb;
+      if ((S & 3) == 0 && q0 + BMQ <= S) {  // 16-byte aligned, whole tile
+        load_lds16(src + q0 + 4 * lane, reinterpret_cast<uint16_t*>(Fd + wave * 2 * BMQ));
+      } else {
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ii = q0 + 4 * lane + e;
-          w[e] = ii < S ? src[ii] : 0.0f;
+          w[e] = ii < S ? src[ii] : 0.0f;  // rows past S: 0, masked
         }
-        *reinterpret_cast<f32x4*>(fl + wave * 2 * BMQ + buf * BMQ + 4 * lane) = w;
+        *reinterpret_cast<f32x4*>(Fd + wave * 2 * BMQ + 4 * lane) = w;
       }
     }
   };
 
-  // Stationary K~ tile and the first q-tile.
+  // Stationary K~ (and V) tiles (2C blocks each, rows past S repeat row S-1)
+  // and the first q-tile.
 #pragma unroll
-  for (int n = 0; n < NKB; ++n) {
-    const int P = 64 * (wave + 4 * n) + lane;
+  for (int n = 0; n < NFB; ++n) {
+    const int blk = wave + 8 * n;
+    const int P = 64 * blk + lane;
     const int row = P / C, ch = (P % C) ^ swz<C>(row);
     const int rr = min(k0 + row, S - 1);
-    load_lds16(kb + (int64_t)rr * ks + 8 * ch, lds + L::KT + 512 * (wave + 4 * n));
+    load_lds16(kb + (int64_t)rr * kstr + 8 * ch, lds + L::KT + 512 * blk);
+    if constexpr (!kRegKV) load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, lds + L::VT + 512 * blk);
   }
-  fetch_q(qt_lo, 0);
-  bf16x8 vreg[D / 16];
+  fetch_q(qt_lo, lds + L::Q0, fl);
+  bf16x8 kreg[kRegKV ? D / 16 : 1], vreg[kRegKV ? D / 16 : 1];
+  if constexpr (kRegKV) {
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    vreg[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    if (j < S)
-      vreg[c] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(vb + (int64_t)j * p.sv.s + 16 * c + 8 * hh));
+    for (int c = 0; c < D / 16; ++c) {
+      vreg[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      if (j < S)
+        vreg[c] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(vb + (int64_t)j * p.sv.s + 16 * c + 8 * hh));
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  bf16x8 kreg[D / 16];
-  {
-    const int row = 32 * wave + ql;
+  if constexpr (kRegKV) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) kreg[c] = lds_read8(lds + L::KT + 8 * tpos<C>(row, 2 * c + hh));
+    for (int c = 0; c < D / 16; ++c)
+      kreg[c] = lds_read8(lds + L::KT + 8 * tpos<C>(32 * kg + ql, 2 * c + hh));
   }
+  const int kq_delta = 32 * C * 8 * (kg - qhalf);  // K~ row 32 kg + ql vs Q~ row 32 qhalf + ql
 
-  // Per-lane LDS offsets (elements) of the row reads and transposed reads.
-  // Row reads (A of S and dP): row 32 qb + ql, chunk 2c + hh.
-  const int rsw = swz<C>(ql);  // rows ql and 32 + ql share the swizzle
-  // Transposed reads of a [rows][C chunks] tile: lane 16g + j16 supplies row
-  // 16 t + 4 hh + j16/4 (+8 for the second read), 4 columns at chunk
-  // 4 db + 2 (g&1) + (j16&3)/2, half (j16&1).
+  // Operand offsets (elements).  Row reads of Q~ / dO (A of S and dP): row
+  // 32 qhalf + ql, chunk 2c + hh.  Transposed reads of a [rows][C chunks]
+  // tile: lane 16g + j16 supplies row 16 t + 4 hh + j16/4 (+8 for the second
+  // read), 4 columns at chunk 4 db + 2 (g&1) + (j16&3)/2, half (j16&1).
+  const int rsw = swz<C>(ql);
   const int trow = 4 * hh + (j16 >> 2);
   const int tch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
   const int thalf = 4 * (j16 & 1);
-  int taddr[2][NB];  // [second read][dim block] element offsets within a [*][D] tile
+  int taddr[2][NB];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int db = 0; db < NB; ++db)
-      taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) + thalf;
-  // dS tiles: [BNK keys][BMQ queries] rows of CS chunks.  dQ A operand:
-  // supplier lane reads key row 16 kc + 8 hh + j16/4 (+4), queries at chunk
-  // 4 qb + 2 (g&1) + (j16&3)/2.
-  const int srow = 8 * hh + (j16 >> 2);
-  int saddr[2][QB];  // [second read (+4 keys)][qb]
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int qb2 = 0; qb2 < QB; ++qb2)
-      saddr[s2][qb2] =
-          8 * ((srow + 4 * s2) * CS + ((4 * qb2 + tch) ^ swz<CS>(srow + 4 * s2))) + thalf;
-  // dQ B operand (K~ transposed): key row 16 kc + 8 hh + j16/4 (+4), dims at
-  // chunk 4 db + 2 (g&1) + (j16&3)/2.
-  int kaddr[2];  // [second read] for this wave's dim block (db = wave)
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-    kaddr[s2] = 8 * ((srow + 4 * s2) * C + ((4 * (wave < NB ? wave : 0) + tch) ^ swz<C>(srow + 4 * s2))) + thalf;
-  // dS write: this lane's key row (32 wave + ql), 4 queries 32 qb + 8 a4 + 4 hh.
-  const int wrow = 32 * wave + ql;
-  const int wsw = swz<CS>(wrow);
+      taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) +
+                      thalf + 32 * qhalf * D;
 
   const float c2 = a.scale_log2;
   const float scale = a.scale;
@@ -373,165 +347,137 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
     dkacc[db] = f32x16{};
   }
 
+  // One q-tile.  The LDS areas come in as distinct restrict pointers so that
+  // the compiler can tell the reads of this tile from the direct-to-LDS loads
+  // of the next one still in flight (otherwise every LDS read would first
+  // wait for all outstanding vector memory operations).
+  auto tile = [&](int qt, const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Gt,
+                  uint16_t* __restrict__ Qn, const uint16_t* __restrict__ KTp,
+                  const uint16_t* __restrict__ VTp, const float* __restrict__ Fc,
+                  float* __restrict__ Fn) {
+    const int q0 = qt * BMQ;
+    const float* nlt = Fc + 32 * qhalf;
+    const float* dlt = Fc + 2 * BMQ + 32 * qhalf;
+    if (qt + 1 < qt_hi) fetch_q(qt + 1, Qn, Fn);
+
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const int off = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
+      const bf16x8 kop = kRegKV ? kreg[kRegKV ? c : 0] : lds_read8(KTp + off + kq_delta);
+      const bf16x8 vop = kRegKV ? vreg[kRegKV ? c : 0] : lds_read8(VTp + off + kq_delta);
+      sacc = mfma32x32x16(lds_read8(Qt + off), kop, sacc);
+      dpacc = mfma32x32x16(lds_read8(Gt + off), vop, dpacc);
+      if (c & 1) __builtin_amdgcn_sched_barrier(0);  // bounds the operand loads in flight
+    }
+
+    // P and dS' = P (dP - Delta) in place (the softmax scale is applied to
+    // dK~ at the end); register r is query q0 + 32 qhalf + 8 (r/4) + 4 hh + r%4.
+    // Tiles off the diagonal and the document edges take the unmasked copy.
+    const int qw0 = q0 + 32 * qhalf;
+    const bool lane_full = (qw0 >= qlo) && (qw0 + 31 <= qhi);
+    auto pds = [&](auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
+      const int lo_off = qlo - qw0 - 4 * hh, hi_off = qhi - qw0 - 4 * hh;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(nlt + 8 * a4 + 4 * hh);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + 8 * a4 + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * a4 + e;
+          const float nl = ALIBI ? n4[e] + slj : n4[e];
+          float pr = fast_exp2(__builtin_fmaf(sacc[r], c2, nl));
+          if (kMasked) {
+            const int io = 8 * a4 + e;
+            if (io < lo_off || io > hi_off) pr = 0.0f;
+          }
+          sacc[r] = pr;
+          dpacc[r] = pr * (dpacc[r] - d4[e]);
+        }
+      }
+    };
+    if (!__all(lane_full)) {
+      asm volatile("" ::: "memory");  // keeps this a branch (no if-conversion)
+      pds(std::true_type{});
+    } else {
+      pds(std::false_type{});
+    }
+
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      float pv[8], sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = sacc[8 * qc + e];
+        sv[e] = dpacc[8 * qc + e];
+      }
+      const bf16x8 pb = pack8(pv);
+      const bf16x8 sb = pack8(sv);
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        const int off = taddr[0][db] + 16 * qc * D;
+        const bf16x8 ga = tr8(Gt + off, taddr[1][db] - taddr[0][db]);
+        const bf16x8 qa = tr8(Qt + off, taddr[1][db] - taddr[0][db]);
+        dvacc[db] = mfma32x32x16(ga, pb, dvacc[db]);
+        dkacc[db] = mfma32x32x16(qa, sb, dkacc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   for (int qt = qt_lo; qt < qt_hi; ++qt) {
     const int buf = (qt - qt_lo) & 1;
-    const int q0 = qt * BMQ;
-    const uint16_t* Qt = lds + L::Q0 + buf * BMQ * D;
-    const uint16_t* Gt = lds + L::G0 + buf * BMQ * D;
-    uint16_t* DSt = lds + L::DS0 + buf * BNK * BMQ;
-    const float* nlt = fl + buf * BMQ;
-    const float* dlt = fl + 2 * BMQ + buf * BMQ;
-    if (qt + 1 < qt_hi) fetch_q(qt + 1, buf ^ 1);
-
-    // Every wave computes every tile (fully masked rows give P = dS = 0): a
-    // skip branch here would split the loop-carried accumulators across paths.
-    {
-      const bool lane_full = (q0 >= qlo) && (q0 + BMQ - 1 <= qhi);
-      const bool need_mask = !__all(lane_full);
-      f32x16 sacc[QB], dpacc[QB];
-#pragma unroll
-      for (int qb2 = 0; qb2 < QB; ++qb2) {
-        sacc[qb2] = f32x16{};
-        dpacc[qb2] = f32x16{};
-      }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2) {
-          const int off = 8 * ((32 * qb2 + ql) * C + ((2 * c + hh) ^ rsw));
-          sacc[qb2] = mfma32x32x16(lds_read8(Qt + off), kreg[c], sacc[qb2]);
-          dpacc[qb2] = mfma32x32x16(lds_read8(Gt + off), vreg[c], dpacc[qb2]);
-        }
-      }
-      // P and dS in place; register r of block qb2 is query
-      // q0 + 32 qb2 + 8 (r/4) + 4 hh + r%4.
-#pragma unroll
-      for (int qb2 = 0; qb2 < QB; ++qb2) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int ioff = 32 * qb2 + 8 * a4 + 4 * hh;
-          const f32x4 n4 = *reinterpret_cast<const f32x4*>(nlt + ioff);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + ioff);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a4 + e;
-            const float nl = ALIBI ? n4[e] + slj : n4[e];
-            float pr = fast_exp2(__builtin_fmaf(sacc[qb2][r], c2, nl));
-            if (need_mask) {
-              const int i = q0 + ioff + e;
-              if (i < qlo || i > qhi) pr = 0.0f;
-            }
-            sacc[qb2][r] = pr;
-            dpacc[qb2][r] = pr * (dpacc[qb2][r] - d4[e]) * scale;
-          }
-        }
-      }
-#pragma unroll
-      for (int qc = 0; qc < BMQ / 16; ++qc) {
-        float pv[8], sv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = sacc[qc >> 1][8 * (qc & 1) + e];
-          sv[e] = dpacc[qc >> 1][8 * (qc & 1) + e];
-        }
-        const bf16x8 pb = pack8(pv);
-        const bf16x8 sb = pack8(sv);
-#pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          const int off = taddr[0][db] + 16 * qc * D;
-          const bf16x8 ga = tr8(Gt + off, taddr[1][db] - taddr[0][db]);
-          const bf16x8 qa = tr8(Qt + off, taddr[1][db] - taddr[0][db]);
-          dvacc[db] = mfma32x32x16(ga, pb, dvacc[db]);
-          dkacc[db] = mfma32x32x16(qa, sb, dkacc[db]);
-        }
-        // dS (same bf16 values) to LDS, row = this lane's key, 4 queries each.
-        const u32x4 w = __builtin_bit_cast(u32x4, sb);
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          const int qoff2 = 16 * qc + 8 * hv + 4 * hh;  // first query of the 4
-          const int ch = qoff2 >> 3;
-          *reinterpret_cast<u32x2*>(DSt + 8 * (wrow * CS + (ch ^ wsw)) + (qoff2 & 7)) =
-              u32x2{w[2 * hv], w[2 * hv + 1]};
-        }
-        // keep the operand reads of one query chunk together (bounds register use)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    tile(qt, lds + L::Q0 + buf * BMQ * D, lds + L::G0 + buf * BMQ * D,
+         lds + L::Q0 + (buf ^ 1) * BMQ * D, lds + L::KT, lds + L::VT, fl + buf * BMQ,
+         fl + (buf ^ 1) * BMQ);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // dQ~ += dS K~ for this tile: wave w < D/32 handles dims 32w..32w+31 for
-    // all the tile's queries (the 32-query blocks share the K~ operand).
-    if (wave < NB) {
-      f32x16 acc[QB];
-#pragma unroll
-      for (int qb2 = 0; qb2 < QB; ++qb2) acc[qb2] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < BNK / 16; ++kc) {
-        const uint16_t* kt2 = lds + L::KT + kaddr[0] + 16 * kc * D;
-        const bf16x8 kb8 = tr8(kt2, kaddr[1] - kaddr[0]);
-#pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2) {
-          const uint16_t* sp = DSt + saddr[0][qb2] + 16 * kc * BMQ;
-          const bf16x8 sa = tr8(sp, saddr[1][qb2] - saddr[0][qb2]);
-          acc[qb2] = mfma32x32x16(sa, kb8, acc[qb2]);
-        }
-        if (kc & 1) __builtin_amdgcn_sched_barrier(0);
-      }
-      float* dst = dqab + (int64_t)(q0 + 4 * hh) * D + 32 * wave + ql;
-      if (q0 + BMQ <= S) {
-#pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            unsafeAtomicAdd(dst + (32 * qb2 + 8 * (r >> 2) + (r & 3)) * D, acc[qb2][r]);
-      } else {
-#pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int io = 32 * qb2 + 8 * (r >> 2) + (r & 3);
-            if (q0 + 4 * hh + io < S) unsafeAtomicAdd(dst + io * D, acc[qb2][r]);
-          }
-      }
-    }
   }
 
-  // Epilogue: stage dK~ and dV (fp32) by key row over the (now idle) tile
-  // areas, then write rows coalesced; dK = R^T dK~.
-  __syncthreads();
-  float* stage = reinterpret_cast<float*>(lds + L::KT);
+  // Epilogue: the two query halves of a key group add their dK~ / dV partial
+  // sums in fp32 over the (now idle) tile areas, then rows are written
+  // coalesced; dK = scale R^T dK~.
+  float* stage = reinterpret_cast<float*>(lds);
   constexpr int FS = D + 4;
-  static_assert(BNK * FS * 2 <= L::F0, "epilogue staging must fit");
+  static_assert(BNK * FS * 4 <= L::F0 * 2, "epilogue staging must fit");
   const int half = a.rd >> 1;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll 1
+    for (int hq = 1; hq >= 0; --hq) {
+      if (qhalf == hq) {
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
+        for (int db = 0; db < NB; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        f32x4 w;
+          for (int a4 = 0; a4 < 4; ++a4) {
+            f32x4* dstp = reinterpret_cast<f32x4*>(stage + (32 * kg + ql) * FS + 32 * db + 8 * a4 +
+                                                   4 * hh);
+            f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pass == 0 ? dkacc[db][4 * a4 + e] : dvacc[db][4 * a4 + e];
-        *reinterpret_cast<f32x4*>(stage + (32 * wave + ql) * FS + 32 * db + 8 * a4 + 4 * hh) = w;
+            for (int e = 0; e < 4; ++e)
+              w[e] = pass == 0 ? dkacc[db][4 * a4 + e] * scale : dvacc[db][4 * a4 + e];
+            if (hq == 0) w += *dstp;
+            *dstp = w;
+          }
       }
-    __syncthreads();
+      __syncthreads();
+    }
     void* outp = pass == 0 ? p.dk : p.dv;
     const Strides so = pass == 0 ? p.sdk : p.sdv;
-    for (int it = tid; it < BNK * (D / 8); it += NT) {
-      const int row = it / (D / 8), d0 = 8 * (it % (D / 8));
+    for (int it = tid; it < BNK * C; it += NT8) {
+      const int row = it / C, d0 = 8 * (it % C);
       const int jj = k0 + row;
       if (jj >= S) continue;
-      const float* srow = stage + row * FS;
+      const float* srow_p = stage + row * FS;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = d0 + e;
-        float y = srow[d];
+        float y = srow_p[d];
         if (pass == 0 && d < a.rd) {
           const bool first = d < half;
           const float2 cs = a.rope[(int64_t)jj * half + (first ? d : d - half)];
-          const float xp = srow[first ? d + half : d - half];
+          const float xp = srow_p[first ? d + half : d - half];
           y = first ? (y * cs.x + xp * cs.y) : (y * cs.x - xp * cs.y);
         }
         x[e] = y;
@@ -550,12 +496,264 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------ dQ
+
+// dQ~ without atomics: one workgroup per (batch, head, 128 queries), four
+// waves of 32 queries.  Q~ and dO stay in registers while K~ and V tiles of 64
+// keys stream through LDS (direct loads, double buffered):
+//   S^T = K~ Q~^T,  dP^T = V dO^T    (A = K~ / V rows from LDS, B = registers)
+//   P = exp2(S scale log2e + nlse_i),  dS' = P (dP - Delta_i)
+//   dQ~^T += K~^T dS'^T               (A = K~ transposed from LDS, B = dS')
+// Lane l owns query l % 32 of its wave, so nlse_i and Delta_i are per-lane
+// scalars.  The epilogue writes dq = scale R^T dQ~.
+constexpr int DQ_BM = 128;  // queries per workgroup
+constexpr int DQ_BN = 64;   // keys per tile
+
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int C = D / 8;
+  constexpr int NB = D / 32;
+  constexpr int TILE = DQ_BN * D;        // elements of one K~ or V tile buffer
+  constexpr int NTB = DQ_BN * C / 64 / 4;  // 1 KB load blocks per wave, per tile and tensor
+  static_assert(C % 4 == 0, "tile blocks must split evenly over 4 waves");
+  constexpr int FS = D + 4;              // epilogue staging row (floats)
+  constexpr int LDS_ELEMS = (4 * TILE > 4 * 32 * FS * 2) ? 4 * TILE : 4 * 32 * FS * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];  // K0 K1 V0 V1
+
+  const AttnShape& a = p.a;
+  const int S = a.S;
+  const int nqt = (S + DQ_BM - 1) / DQ_BM;
+  const int BH = a.B * a.H;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest q-tile first, heads fastest
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int q0 = qt * DQ_BM;
+  const int qi = q0 + 32 * wave + ql;  // this lane's query
+  const int qc = qi < S ? qi : S - 1;
+
+  const bool rot = a.rd > 0;
+  const uint16_t* qb = rot ? p.qrot + (int64_t)bh * S * D
+                           : (const uint16_t*)p.q + b * p.sq.b + h * p.sq.h;
+  const int64_t qstr = rot ? D : p.sq.s;
+  const uint16_t* kb = rot ? p.krot + (int64_t)bh * S * D
+                           : (const uint16_t*)p.k + b * p.sk.b + h * p.sk.h;
+  const int64_t kstr = rot ? D : p.sk.s;
+  const uint16_t* vb = (const uint16_t*)p.v + b * p.sv.b + h * p.sv.h;
+  const uint16_t* gb = (const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h;
+
+  // Allowed keys of this lane's query: [lo, hi]; keys any query of the block may see.
+  const int32_t* drow = a.docs ? a.docs + (int64_t)b * (a.n_docs + 1) : nullptr;
+  int lo = 0, hi = S - 1;
+  if (drow) {
+    int ds, de;
+    doc_bounds(drow, a.n_docs, S, qc, ds, de);
+    lo = ds;
+    hi = de - 1;
+  }
+  if (a.causal && qi < hi) hi = qi;
+  const int qlast = (q0 + DQ_BM - 1 < S - 1) ? q0 + DQ_BM - 1 : S - 1;
+  int blo = 0, bhi = S - 1;
+  if (drow) {
+    int s0, e0, s1, e1;
+    doc_bounds(drow, a.n_docs, S, q0, s0, e0);
+    doc_bounds(drow, a.n_docs, S, qlast, s1, e1);
+    blo = s0;
+    bhi = e1 - 1;
+  }
+  if (a.causal && qlast < bhi) bhi = qlast;
+  const int kt_lo = blo / DQ_BN, kt_hi = bhi / DQ_BN + 1;
+
+  // Tile loader: rows [k0, k0 + 64) of K~ and V (rows past S repeat row S-1,
+  // their keys are masked).  Position P = 64 * blk + lane of a tile -> (row
+  // P / C, chunk (P % C) ^ swizzle(row)); this wave loads blocks wave + 4 n.
+  int koff[NTB], voff[NTB];
+#pragma unroll
+  for (int n = 0; n < NTB; ++n) {
+    const int P = 64 * (wave + 4 * n) + lane;
+    const int row = P / C, ch = (P % C) ^ swz<C>(row);
+    koff[n] = (int)(row * kstr) + 8 * ch;
+    voff[n] = (int)(row * p.sv.s) + 8 * ch;
+  }
+  auto fetch = [&](int kt, uint16_t* Kd, uint16_t* Vd) {
+    const int k0 = kt * DQ_BN;
+    if (k0 + DQ_BN <= S) {
+      const uint16_t* kt0 = kb + (int64_t)k0 * kstr;
+      const uint16_t* vt0 = vb + (int64_t)k0 * p.sv.s;
+#pragma unroll
+      for (int n = 0; n < NTB; ++n) {
+        load_lds16(kt0 + koff[n], Kd + 512 * (wave + 4 * n));
+        load_lds16(vt0 + voff[n], Vd + 512 * (wave + 4 * n));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NTB; ++n) {
+        const int P = 64 * (wave + 4 * n) + lane;
+        const int row = P / C, ch = (P % C) ^ swz<C>(row);
+        const int rr = min(k0 + row, S - 1);
+        load_lds16(kb + (int64_t)rr * kstr + 8 * ch, Kd + 512 * (wave + 4 * n));
+        load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, Vd + 512 * (wave + 4 * n));
+      }
+    }
+  };
+  fetch(kt_lo, lds, lds + 2 * TILE);
+
+  // Q~ and dO of this lane's query as B operands: chunk c holds dims 16c + 8hh .. +7.
+  bf16x8 qreg[D / 16], greg[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const int d0 = 16 * c + 8 * hh;
+    u32x4 wq = *reinterpret_cast<const u32x4*>(qb + (int64_t)qc * qstr + d0);
+    u32x4 wg = *reinterpret_cast<const u32x4*>(gb + (int64_t)qc * p.sdo.s + d0);
+    if (qi >= S) wq = wg = u32x4{0u, 0u, 0u, 0u};
+    qreg[c] = __builtin_bit_cast(bf16x8, wq);
+    greg[c] = __builtin_bit_cast(bf16x8, wg);
+  }
+  const float nl = qi < S ? p.nlse[(int64_t)bh * S + qi] : 0.0f;
+  const float dl = qi < S ? p.delta[(int64_t)bh * S + qi] : 0.0f;
+  const float c2 = a.scale_log2;
+  const float sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
+
+  // LDS operand offsets.  Row reads (A of S^T and dP^T): row 32 blk + ql,
+  // chunk 2c + hh.  Transposed K~ reads (A of dQ~^T): lane 16g + j16 supplies
+  // key row 16 kc + 4 hh + j16/4 (+8 for the second read), 4 dims at chunk
+  // 4 db + 2 (g&1) + (j16&3)/2, half (j16&1).
+  const int rsw = swz<C>(ql);
+  const int trow = 4 * hh + (j16 >> 2);
+  const int tch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int thalf = 4 * (j16 & 1);
+  int taddr[2][NB];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+      taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) + thalf;
+
+  f32x16 dqacc[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) dqacc[db] = f32x16{};
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // One key tile; restrict pointers let the compiler separate these reads from
+  // the next tile's direct loads in flight.
+  auto step = [&](int kt, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
+                  uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
+    const int k0 = kt * DQ_BN;
+    if (kt + 1 < kt_hi) fetch(kt + 1, Kn, Vn);
+    const bool lane_any = (k0 <= hi) && (k0 + DQ_BN - 1 >= lo);
+    if (!__any(lane_any)) return;
+    const bool lane_full = (k0 >= lo) && (k0 + DQ_BN - 1 <= hi);
+    const bool masked = !__all(lane_full);
+    // The tile's two 32-key halves one after the other (bounds the registers).
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int off = 8 * (ql * C + ((2 * c + hh) ^ rsw)) + 32 * blk * D;
+        sacc = mfma32x32x16(lds_read8(Kc + off), qreg[c], sacc);
+        dpacc = mfma32x32x16(lds_read8(Vc + off), greg[c], dpacc);
+        if (c & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      // Register r: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.
+      auto pds = [&](auto mk) {
+        constexpr bool kMasked = decltype(mk)::value;
+        const int jlo = lo - k0 - 32 * blk - 4 * hh, jhi = hi - k0 - 32 * blk - 4 * hh;
+        const float kbase = ALIBI ? sl2 * (float)(k0 + 32 * blk + 4 * hh) + nl : nl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 8 * (r >> 2) + (r & 3);
+          const float bias = ALIBI ? kbase + sl2 * (float)ko : nl;
+          float pr = fast_exp2(__builtin_fmaf(sacc[r], c2, bias));
+          if (kMasked && (ko < jlo || ko > jhi)) pr = 0.0f;
+          dpacc[r] = pr * (dpacc[r] - dl);
+        }
+      };
+      if (masked) {
+        asm volatile("" ::: "memory");  // keeps this a branch (no if-conversion)
+        pds(std::true_type{});
+      } else {
+        pds(std::false_type{});
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = dpacc[8 * kh + e];
+        const bf16x8 sb = pack8(sv);
+        const int kc = 2 * blk + kh;
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const bf16x8 ka = tr8(Kc + taddr[0][db] + 16 * kc * D, taddr[1][db] - taddr[0][db]);
+          dqacc[db] = mfma32x32x16(ka, sb, dqacc[db]);
+        }
+      }
+    }
+  };
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    const int buf = (kt - kt_lo) & 1;
+    step(kt, lds + buf * TILE, lds + (2 + buf) * TILE, lds + (1 - buf) * TILE,
+         lds + (3 - buf) * TILE);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Epilogue: stage this wave's 32 rows of dQ~ (fp32) in LDS, then write
+  // dq = scale R^T dQ~ row-wise.  Register r of dim block db holds dim
+  // 32 db + 8 (r/4) + 4 hh + r%4 of query ql.
+  float* stage = reinterpret_cast<float*>(lds) + wave * 32 * FS;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = dqacc[db][4 * a4 + e];
+      *reinterpret_cast<f32x4*>(stage + ql * FS + 32 * db + 8 * a4 + 4 * hh) = w;
+    }
+  lds_wave_sync();
+  const float scale = a.scale;
+  const int rd = a.rd, half = rd >> 1;
+  for (int it = lane; it < 32 * C; it += 64) {
+    const int row = it / C, d0 = 8 * (it % C);
+    const int i = q0 + 32 * wave + row;
+    if (i >= S) continue;
+    const float* srow = stage + row * FS;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      float y = srow[d];
+      if (d < rd) {
+        const bool first = d < half;
+        const float2 cs = a.rope[(int64_t)i * half + (first ? d : d - half)];
+        const float xp = srow[first ? d + half : d - half];
+        y = first ? (y * cs.x + xp * cs.y) : (y * cs.x - xp * cs.y);
+      }
+      x[e] = y * scale;
+    }
+    if (p.out_f32) {
+      float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+      *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    } else {
+      uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+      *reinterpret_cast<u32x4*>(orow) =
+          u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+    }
+  }
+}
+
 // ------------------------------------------------------------------ finalize
 
 // dq = R^T dQ~ (rotation by -theta), cast to the output type.  Row groups as
 // in the prep pass; rotary partners are exchanged through LDS.
 template <int D>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32) {
+__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32,
+                                                          float dq_scale) {
   using RG = RowGroups<D>;
   constexpr int C = RG::C, G = RG::G, RPW = RG::RPW;
   __shared__ __attribute__((aligned(16))) float rowbuf[4][RPW][D];
@@ -589,6 +787,8 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f
   float x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    lo[e] *= dq_scale;
+    hi[e] *= dq_scale;
     x[e] = lo[e];
     x[4 + e] = hi[e];
   }
@@ -636,15 +836,19 @@ hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
-  const int nkt = (p.a.S + BNK - 1) / BNK;
-  const dim3 grid((unsigned)(nkt * p.a.B * p.a.H));
+  const unsigned BH = (unsigned)(p.a.B * p.a.H);
+  const dim3 kgrid((unsigned)((p.a.S + BNK - 1) / BNK) * BH);
   if (p.a.alibi)
-    hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(NT8), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(NT8), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_finalize_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p, p.out_f32);
+  const dim3 qgrid((unsigned)((p.a.S + DQ_BM - 1) / DQ_BM) * BH);
+  if (p.a.alibi)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(NT), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev, 3, st);
 }
@@ -660,11 +864,12 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t*
   }
 }
 
-hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32) {
+hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, float dq_scale) {
+  const dim3 blk(256);
   switch (p.a.D) {
-    case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), row_grid<64>(p), dim3(256), 0, st, p, out_f32); break;
-    case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), row_grid<96>(p), dim3(256), 0, st, p, out_f32); break;
-    case 128: hipLaunchKernelGGL((dq_finalize_kernel<128>), row_grid<128>(p), dim3(256), 0, st, p, out_f32); break;
+    case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), row_grid<64>(p), blk, 0, st, p, out_f32, dq_scale); break;
+    case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), row_grid<96>(p), blk, 0, st, p, out_f32, dq_scale); break;
+    case 128: hipLaunchKernelGGL((dq_finalize_kernel<128>), row_grid<128>(p), blk, 0, st, p, out_f32, dq_scale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

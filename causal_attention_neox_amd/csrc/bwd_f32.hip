@@ -290,7 +290,7 @@ hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* 
   }
   if (e != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  if ((e = launch_dq_finalize(p, st, 1)) != hipSuccess) return e;
+  if ((e = launch_dq_finalize(p, st, 1, 1.0f)) != hipSuccess) return e;
   return record_event(ev, 3, st);
 }
 

@@ -50,7 +50,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;   // [B][H][S][D] fp32 workspace (contiguous)
+  float* dq_acc;   // [B][H][S][D] fp32 workspace (contiguous; fp32 path only)
   float* delta;    // [B][H][S] fp32 workspace: dO_i . o_i
   float* nlse;     // [B][H][S] fp32 workspace: -lse_i * log2(e) (ALiBi: also - slope * log2(e) * i)
   uint16_t* qrot;  // [B][H][S][D] bf16 workspace: rotated q (bf16 path with rotary)
@@ -68,12 +68,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t*
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
 
 // `ev` is null or 4 events recorded before the preprocess kernel, after it,
-// after the main kernel(s) and after the dq finalize.
+// after the dK/dV kernel and at the end (after the dQ kernel or finalize).
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 
-// dq = R^T dQ~ from the fp32 accumulator, cast; shared by both paths.
-hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32);
+// dq = dq_scale * R^T dQ~ from the fp32 accumulator, cast; shared by both paths
+// (the bf16 path accumulates dS without the softmax scale and passes it here).
+hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, float dq_scale);
 
 inline hipError_t record_event(const hipEvent_t* ev, int i, hipStream_t st) {
   return ev ? hipEventRecord(ev[i], st) : hipSuccess;

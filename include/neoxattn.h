@@ -110,9 +110,9 @@ typedef struct neox_strides {
  *                forward records [0] before its first kernel, [1] after the q/k
  *                rotation pass (right after [0] when none runs) and [2] after
  *                the attention kernel; the backward records [0] before the
- *                preprocess kernel, [1] after it, [2] after the main kernel(s)
- *                and [3] after the dq finalize.  The events are owned by the
- *                caller.
+ *                preprocess kernel, [1] after it, [2] after the dK/dV kernel
+ *                and [3] at its end (after the dQ kernel, or the fp32 path's
+ *                dq finalize).  The events are owned by the caller.
  */
 typedef struct neox_attn_args {
   int B, H, S, D;
@@ -175,8 +175,9 @@ size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
  * `dtype`) are written and must not alias the inputs.  workspace: device
  * memory of at least neox_rope_attn_bwd_workspace_size() bytes, 256-byte
  * aligned, owned by the caller, overwritten by the call (its contents
- * afterwards are unspecified).  dq is accumulated with fp32 atomics, so its
- * last bits may differ from run to run; dk and dv are deterministic.
+ * afterwards are unspecified).  The bf16 path is deterministic (dq, dk and dv
+ * are each reduced by one workgroup, in a fixed order); the fp32 path
+ * accumulates dq with fp32 atomics, so its last bits may vary run to run.
  */
 int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
