@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-fwd-target", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with a plain 1 GiB device copy (scale for traffic counters)")
     return ap.parse_args()
 
 
@@ -60,6 +62,29 @@ def make_events(torch, n):
     for e in evs:
         e.record()  # creates the underlying hipEvent_t
     return evs
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.json
+    (FETCH_SIZE and WRITE_SIZE counters scaled by a plain copy), or None when
+    absent or when the kernel's sources changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            ent = json.load(f)["kernels"][kernel]
+        if ent["workload"] != workload or source_digest(ent["sources"]) != ent["sources_sha256"]:
+            return None
+        return int(ent["fetch_bytes"] + ent["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def run_gpu(args, torch, np, neox, W, wl, inp):
@@ -114,22 +139,28 @@ def fwd_target(args, torch, np, neox, W):
     fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                       device="cuda")
     n = max(args.steps, 20)
-    events = [make_events(torch, 3) for _ in range(n)]
-    call = lambda ev: neox.neox_attn_fwd_ex(q, k, v, o, lse, rotary_dim=wl.rotary_dim,  # noqa
-                                            rope_base=wl.rope_base, causal=True,
-                                            softmax_scale=wl.softmax_scale, workspace=fws,
-                                            phase_events=ev)
+    call = lambda ev=None: neox.neox_attn_fwd_ex(  # noqa: E731
+        q, k, v, o, lse, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=True,
+        softmax_scale=wl.softmax_scale, workspace=fws, phase_events=ev)
     for _ in range(args.warmup):
-        call(events[0])
+        call()
     start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
     for i in range(n):
-        call(events[i])
+        call()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / n
-    ms_attn = sum(ev[1].elapsed_time(ev[2]) for ev in events) / n
+    # Split into rotation pass and attention kernel: one reused event set, read
+    # after each call (recording many live events slows the host down).
+    ev = make_events(torch, 3)
+    ms_attn = 0.0
+    for i in range(n):
+        call(ev)
+        torch.cuda.synchronize()
+        ms_attn += ev[1].elapsed_time(ev[2])
+    ms_attn /= n
     flops = 4 * wl.D * W.total_pairs(inp)
     tf = flops / (ms * 1e-3) / 1e12
     tf_attn = flops / (ms_attn * 1e-3) / 1e12
@@ -182,9 +213,9 @@ def _head64(W, inp, name, b, h):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(heads shard across GPUs with no exchange; see the design "
-                                   "notes)"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 (attention "
+                                   "heads are independent: N GPUs would each run B*H/N heads "
+                                   "with no communication)"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -249,12 +280,13 @@ def main():
     if kd["bound"] == "mfma":
         ach = kd["flops"] / (kd["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": dom}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, wl.name), "kernel": dom}
     else:
         ach = kd["bytes"] / (kd["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, wl.name),
+                "kernel": dom}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -274,6 +306,11 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, np, W, wl, inp)
     print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -195,8 +195,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   const AttnShape& a = p.a;
   const int S = a.S;
   const int BH = a.B * a.H;
-  const int kt = (int)(blockIdx.x / BH);  // small kt = most queries: heaviest first
-  const int bh = (int)(blockIdx.x % BH);
+  int kt, bh;  // kt 0 (most queries) first; Q~ and dO of a head: 4 S D bytes
+  xcd_order((S + BNK - 1) / BNK, BH, (int64_t)4 * S * D, kt, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kg = wave & 3, qhalf = wave >> 2;

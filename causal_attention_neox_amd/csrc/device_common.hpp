@@ -101,6 +101,34 @@ __device__ __forceinline__ void rotate8_scalar(const uint16_t* row, int d0, floa
   }
 }
 
+// Workgroup order for kernels that stream one head's K/V (or Q/dO) tiles
+// from many workgroups (one per row tile).  Workgroups go to the 8 XCDs
+// round-robin (workgroup i on XCD i % 8), each XCD with its own 4 MB L2.
+// When B*H is a multiple of 8 every workgroup of head bh runs on XCD bh % 8,
+// and each XCD takes its heads in groups small enough that the group's
+// streamed tiles (stream_bytes per head) stay L2-resident while all row tiles
+// of the group are in flight, heaviest tile first.  Otherwise heads run
+// fastest, heaviest tile level first.  Returns (tile, bh); tile 0 is the
+// heaviest.
+__device__ __forceinline__ void xcd_order(int ntile, int BH, int64_t stream_bytes, int& tile,
+                                          int& bh) {
+  const int i = (int)blockIdx.x;
+  if ((BH & 7) == 0) {
+    const int x = i & 7, jj = i >> 3;
+    const int hpx = BH >> 3;  // heads per XCD
+    int G = (int)(((int64_t)5 << 19) / (stream_bytes > 0 ? stream_bytes : 1));  // 2.5 MB
+    G = G < 1 ? 1 : (G > hpx ? hpx : G);
+    const int g = jj / (ntile * G);
+    const int gs = (hpx - g * G) < G ? hpx - g * G : G;
+    const int rem = jj - g * ntile * G;
+    tile = rem / gs;
+    bh = 8 * (g * G + rem % gs) + x;
+  } else {
+    tile = i / BH;
+    bh = i % BH;
+  }
+}
+
 // Per-row passes (q/k rotation, backward prep and finalize) give each row a
 // group of G lanes, G = D/8 rounded up to a power of two, 16 B per lane, so
 // one wave covers 64/G rows and every memory instruction is full width.  Each

@@ -25,7 +25,10 @@
 //    max is raised lazily (only when a row's max grows by more than 2^8 in the
 //    exp2 domain), so O and the row sum are rescaled rarely.
 //  * Workgroups are issued heaviest q-tile first, heads fastest: with B*H a
-//    multiple of 8 all q-tiles of a head share one XCD and its L2.
+//    multiple of 8 all q-tiles of a head share one XCD and its L2.  (Grouping
+//    each XCD's heads so that their K/V stay L2-resident cuts the fetched
+//    bytes five-fold but measured slower here: the K/V re-reads are served by
+//    the 256 MB Infinity Cache, and the kernel is bound by issue, not memory.)
 //  * With a caller workspace, a row pass first writes q~ = R q and k~ = R k
 //    (the NeoX pipeline rotates q and k before attention), and the attention
 //    kernel runs its rotation-free form on them.  Without one, Q~ is rotated
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   const int S = a.S;
   const int nqt = (S + BM - 1) / BM;
   const int BH = a.B * a.H;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest q-tile first, heads fastest
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
