@@ -87,7 +87,7 @@ struct TilePlan {
   static constexpr int NPAIR = PAIRS ? (BN * D / (2 * W) + NT - 1) / NT : 1;
   static constexpr int NREG = ROT == 3 ? BN * CPR / NT : 1;
   int kdirect;            // bit i: this lane's K position of block i is loaded directly
-  int koff[NB], voff[NB]; // row * stride + 8 * chunk
+  uint32_t koff[NB], voff[NB];  // byte offsets (row * stride + 8 * chunk) * 2 from the tile start
   int pitem[NPAIR];       // row << 8 | p0, -1 unused
   int plds[NPAIR];        // LDS element offsets of dims p0.. (low 16 bits) and half+p0..
   u32x4 plo[NPAIR], phi[NPAIR];
@@ -109,8 +109,8 @@ struct TilePlan {
       const int ck = (P % CPR) ^ Swz<D>::k(row);
       const int cv = (P % CPR) ^ Swz<D>::v(row);
       if (ck >= rchunks) kdirect |= 1 << i;
-      koff[i] = (int)(row * ks) + 8 * ck;
-      voff[i] = (int)(row * vs) + 8 * cv;
+      koff[i] = 2u * (uint32_t)(row * ks + 8 * ck);
+      voff[i] = 2u * (uint32_t)(row * vs + 8 * cv);
     }
     const int half = rd >> 1;
     const int slots = PAIRS ? half / W : 0;
@@ -146,8 +146,11 @@ struct TilePlan {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int blk = wave + 4 * i;
-        load_lds16(vt0 + voff[i], Vt + 512 * blk);
-        if (kdirect & (1 << i)) load_lds16(kt0 + koff[i], Kt + 512 * blk);
+        // uniform tile base + 32-bit per-lane byte offset: the scalar-base
+        // addressing form, no 64-bit address arithmetic per load
+        load_lds16(reinterpret_cast<const char*>(vt0) + voff[i], Vt + 512 * blk);
+        if (kdirect & (1 << i))
+          load_lds16(reinterpret_cast<const char*>(kt0) + koff[i], Kt + 512 * blk);
       }
     } else {
       // last tile: rows past S re-read row S-1 (their keys are masked)
@@ -283,10 +286,19 @@ struct FwdState {
       const bool lane_full = (k0 >= lo) && (k0 + BN - 1 <= hi);
       const bool need_mask = !__all(lane_full);
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      // K~ operands are read one dims step ahead of the MFMAs using them.
+      bf16x8 k0c = lds_read8(lds + kaddr[0]), k1c = lds_read8(lds + kaddr[0] + 32 * D);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        sacc[0] = mfma32x32x16(lds_read8(lds + kaddr[c]), qreg[c], sacc[0]);
-        sacc[1] = mfma32x32x16(lds_read8(lds + kaddr[c] + 32 * D), qreg[c], sacc[1]);
+        bf16x8 k0n = k0c, k1n = k1c;
+        if (c + 1 < D / 16) {
+          k0n = lds_read8(lds + kaddr[c + 1]);
+          k1n = lds_read8(lds + kaddr[c + 1] + 32 * D);
+        }
+        sacc[0] = mfma32x32x16(k0c, qreg[c], sacc[0]);
+        sacc[1] = mfma32x32x16(k1c, qreg[c], sacc[1]);
+        k0c = k0n;
+        k1c = k1n;
       }
       // Register r of block blk: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.  The
       // scores stay in the accumulator registers: raw (RoPE) or exp2-domain
@@ -334,21 +346,28 @@ struct FwdState {
           sacc[blk][r] = ALIBI ? fast_exp2(x - m_use) : fast_exp2(__builtin_fmaf(x, c2, -m_use));
           l_run += sacc[blk][r];
         }
+      // V^T operands are read one MFMA ahead of their use.
+      constexpr int NDB = D / 32, NG = (BN / 16) * NDB;
+      auto vread = [&](int g) {
+        const uint16_t* vp = lds + vaddr[g % NDB] + 16 * (g / NDB) * 8 * CPR;
+        const s16x4 v0 = lds_read_tr4(vp);
+        const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 pb[BN / 16];
 #pragma unroll
       for (int cp = 0; cp < BN / 16; ++cp) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = sacc[cp >> 1][8 * (cp & 1) + e];
-        const bf16x8 pb = pack8(pv);
+        pb[cp] = pack8(pv);
+      }
+      bf16x8 vcur = vread(0);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vp = lds + vaddr[db] + 16 * cp * 8 * CPR;
-          const s16x4 v0 = lds_read_tr4(vp);
-          const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = mfma32x32x16(va, pb, oacc[db]);
-        }
+      for (int g = 0; g < NG; ++g) {
+        const bf16x8 vnext = g + 1 < NG ? vread(g + 1) : vcur;
+        oacc[g % NDB] = mfma32x32x16(vcur, pb[g / NDB], oacc[g % NDB]);
+        vcur = vnext;
       }
     }
     if (more) tp.store(Kn, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
@@ -362,10 +381,18 @@ struct FwdState {
   }
 };
 
+// Workgroups per CU the register budget is sized for: 3 (at most 168
+// registers per lane) for the plain-K form at D <= 96, else 2.  The rotating
+// forms need more registers.
+template <int D, int ROT>
+struct FwdOccupancy {
+  static constexpr int value = (ROT == 0 && D <= 96) ? 3 : 2;
+};
+
 // ROT: how K tiles are staged (0: plain or pre-rotated K; 1, 2: rotary pair
 // items; 3: every chunk through registers).  QROT: rotate Q~ at load.
 template <int D, int ROT, bool ALIBI, bool QROT>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_kernel(FwdParams p) {
   constexpr int CPR = D / 8;
   constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
@@ -377,7 +404,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest q-tile first, heads fastest
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
   const int ql = lane & 31, hh = lane >> 5;
   const int q0 = qt * BM;
 
