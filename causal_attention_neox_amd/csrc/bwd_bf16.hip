@@ -361,14 +361,29 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (qt + 1 < qt_hi) fetch_q(qt + 1, Qn, Fn);
 
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // Operands of dims step c: Q~ and dO rows (and K~ / V rows from LDS),
+    // read one step ahead of the MFMAs that use them.
+    struct Ops {
+      bf16x8 q, g, k, v;
+    };
+    auto ops = [&](int c) {
+      const int off = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
+      Ops o;
+      o.q = lds_read8(Qt + off);
+      o.g = lds_read8(Gt + off);
+      if constexpr (!kRegKV) {
+        o.k = lds_read8(KTp + off + kq_delta);
+        o.v = lds_read8(VTp + off + kq_delta);
+      }
+      return o;
+    };
+    Ops cur = ops(0);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const int off = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
-      const bf16x8 kop = kRegKV ? kreg[kRegKV ? c : 0] : lds_read8(KTp + off + kq_delta);
-      const bf16x8 vop = kRegKV ? vreg[kRegKV ? c : 0] : lds_read8(VTp + off + kq_delta);
-      sacc = mfma32x32x16(lds_read8(Qt + off), kop, sacc);
-      dpacc = mfma32x32x16(lds_read8(Gt + off), vop, dpacc);
-      if (c & 1) __builtin_amdgcn_sched_barrier(0);  // bounds the operand loads in flight
+      const Ops nxt = c + 1 < D / 16 ? ops(c + 1) : cur;
+      sacc = mfma32x32x16(cur.q, kRegKV ? kreg[kRegKV ? c : 0] : cur.k, sacc);
+      dpacc = mfma32x32x16(cur.g, kRegKV ? vreg[kRegKV ? c : 0] : cur.v, dpacc);
+      cur = nxt;
     }
 
     // P and dS' = P (dP - Delta) in place (the softmax scale is applied to
@@ -404,6 +419,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       pds(std::false_type{});
     }
 
+    bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       float pv[8], sv[8];
@@ -412,17 +428,24 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
         pv[e] = sacc[8 * qc + e];
         sv[e] = dpacc[8 * qc + e];
       }
-      const bf16x8 pb = pack8(pv);
-      const bf16x8 sb = pack8(sv);
+      pb[qc] = pack8(pv);
+      sb[qc] = pack8(sv);
+    }
+    // dO^T and Q~^T operands of (query chunk, dim block) g, read one MFMA
+    // pair ahead of their use.
+    constexpr int NG = 2 * NB;
+    auto tops = [&](int g) {
+      const int off = taddr[0][g % NB] + 16 * (g / NB) * D;
+      const int second = taddr[1][g % NB] - taddr[0][g % NB];
+      return Ops{tr8(Qt + off, second), tr8(Gt + off, second), bf16x8{}, bf16x8{}};
+    };
+    Ops tc = tops(0);
 #pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        const int off = taddr[0][db] + 16 * qc * D;
-        const bf16x8 ga = tr8(Gt + off, taddr[1][db] - taddr[0][db]);
-        const bf16x8 qa = tr8(Qt + off, taddr[1][db] - taddr[0][db]);
-        dvacc[db] = mfma32x32x16(ga, pb, dvacc[db]);
-        dkacc[db] = mfma32x32x16(qa, sb, dkacc[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < NG; ++g) {
+      const Ops tn = g + 1 < NG ? tops(g + 1) : tc;
+      dvacc[g % NB] = mfma32x32x16(tc.g, pb[g / NB], dvacc[g % NB]);
+      dkacc[g % NB] = mfma32x32x16(tc.q, sb[g / NB], dkacc[g % NB]);
+      tc = tn;
     }
   };
   for (int qt = qt_lo; qt < qt_hi; ++qt) {
@@ -651,12 +674,22 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // K~ / V rows of dims step c, read one step ahead of their MFMAs.
+      auto rows = [&](int c, bf16x8& kr, bf16x8& vr) {
+        const int off = 8 * (ql * C + ((2 * c + hh) ^ rsw)) + 32 * blk * D;
+        kr = lds_read8(Kc + off);
+        vr = lds_read8(Vc + off);
+      };
+      bf16x8 kc_, vc_;
+      rows(0, kc_, vc_);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const int off = 8 * (ql * C + ((2 * c + hh) ^ rsw)) + 32 * blk * D;
-        sacc = mfma32x32x16(lds_read8(Kc + off), qreg[c], sacc);
-        dpacc = mfma32x32x16(lds_read8(Vc + off), greg[c], dpacc);
-        if (c & 1) __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kn = kc_, vn = vc_;
+        if (c + 1 < D / 16) rows(c + 1, kn, vn);
+        sacc = mfma32x32x16(kc_, qreg[c], sacc);
+        dpacc = mfma32x32x16(vc_, greg[c], dpacc);
+        kc_ = kn;
+        vc_ = vn;
       }
       // Register r: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.
       auto pds = [&](auto mk) {
@@ -678,18 +711,26 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
       } else {
         pds(std::false_type{});
       }
+      bf16x8 sb[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[e] = dpacc[8 * kh + e];
-        const bf16x8 sb = pack8(sv);
-        const int kc = 2 * blk + kh;
+        sb[kh] = pack8(sv);
+      }
+      // K~^T operand of (key chunk, dim block) g, read one MFMA ahead.
+      constexpr int NG = 2 * NB;
+      auto kt_op = [&](int g) {
+        const int kc = 2 * blk + g / NB, db = g % NB;
+        return tr8(Kc + taddr[0][db] + 16 * kc * D, taddr[1][db] - taddr[0][db]);
+      };
+      bf16x8 ka = kt_op(0);
 #pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          const bf16x8 ka = tr8(Kc + taddr[0][db] + 16 * kc * D, taddr[1][db] - taddr[0][db]);
-          dqacc[db] = mfma32x32x16(ka, sb, dqacc[db]);
-        }
+      for (int g = 0; g < NG; ++g) {
+        const bf16x8 kn = g + 1 < NG ? kt_op(g + 1) : ka;
+        dqacc[g % NB] = mfma32x32x16(ka, sb[g / NB], dqacc[g % NB]);
+        ka = kn;
       }
     }
   };
