@@ -275,3 +275,42 @@ def attn_bwd(q, k, v, dout, *, rotary_dim: int, rope_base: float = 10000.0,
                 out[4].reshape(B, H, S, D))
     return tuple(out)
 
+
+
+# --------------------------------------------------------------------------
+# Autoregressive decoding (one new token against a key/value cache)
+# --------------------------------------------------------------------------
+
+def attn_decode(q, k, v, k_cache, v_cache, *, rotary_dim: int, rope_base: float = 10000.0,
+                softmax_scale: Optional[float] = None):
+    """One decoding step of one head.
+
+    The FasterTransformer GPT-NeoX guide ("FasterTransformer GPT-NeoX 推理指南",
+    section "背景") separates the context decoder from a decoder that generates
+    one token at a time against the earlier tokens.  Read plainly, one step is
+    the last row of causal attention over the sequence so far: the new token
+    sits at position t = len(k_cache); its query and key are rotated at that
+    position (R1-R3); its rotated key and its value join the cache; its query
+    attends over all t + 1 cached tokens.  The cache holds keys already rotated,
+    each at its own position, as a decoder stores them.
+
+    q, k, v: [D] float64, the new token's projections (not rotated).
+    k_cache, v_cache: [t, D] float64 (rotated keys; values).
+    Returns (o [D], lse, k_rot [D]): the output, the natural-log logsumexp of
+    the t + 1 scores, and the rotated key appended to the cache.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    D = q.shape[-1]
+    t = int(np.asarray(k_cache).shape[0])
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    pos = np.array([t])
+    q_rot = rope_rotate(q[None, :], pos, rotary_dim, rope_base)[0]
+    k_rot = rope_rotate(np.asarray(k, dtype=np.float64)[None, :], pos, rotary_dim, rope_base)[0]
+    keys = np.concatenate([np.asarray(k_cache, dtype=np.float64).reshape(t, D), k_rot[None, :]])
+    vals = np.concatenate([np.asarray(v_cache, dtype=np.float64).reshape(t, D),
+                           np.asarray(v, dtype=np.float64)[None, :]])
+    s = scale * (keys @ q_rot)
+    m = s.max()
+    e = np.exp(s - m)
+    l = e.sum()
+    return (e / l) @ vals, m + np.log(l), k_rot

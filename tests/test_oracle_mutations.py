@@ -13,7 +13,7 @@ from tests import test_oracle_pins as pins
 
 ORIG = {n: getattr(orc, n) for n in
         ("rope_rotate", "rope_inv_freq", "allowed_mask", "alibi_bias", "_head_probs",
-         "head_backward", "head_forward", "alibi_slopes")}
+         "head_backward", "head_forward", "alibi_slopes", "attn_decode")}
 
 
 def _rotate_sign_flipped(x, positions, rotary_dim, base, inverse=False):
@@ -105,6 +105,23 @@ def _forward_k_unrotated(q, k, v, *, rotary_dim, rope_base, causal, scale, slope
     return P @ v, lse
 
 
+def _decode_position_off_by_one(q, k, v, k_cache, v_cache, *, rotary_dim, rope_base=10000.0,
+                                softmax_scale=None):
+    t = int(np.asarray(k_cache).shape[0])
+    D = np.asarray(q).shape[-1]
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    pos = np.array([max(t - 1, 0)])  # slip: the previous token's position
+    qr = orc.rope_rotate(np.asarray(q, dtype=np.float64)[None], pos, rotary_dim, rope_base)[0]
+    kr = orc.rope_rotate(np.asarray(k, dtype=np.float64)[None], pos, rotary_dim, rope_base)[0]
+    keys = np.concatenate([np.asarray(k_cache, dtype=np.float64).reshape(t, D), kr[None]])
+    vals = np.concatenate([np.asarray(v_cache, dtype=np.float64).reshape(t, D),
+                           np.asarray(v, dtype=np.float64)[None]])
+    s = scale * (keys @ qr)
+    m = s.max()
+    e = np.exp(s - m)
+    return (e / e.sum()) @ vals, m + np.log(e.sum()), kr
+
+
 MUTATIONS = {
     "rotation_sign": ("rope_rotate", _rotate_sign_flipped),
     "rotation_interleaved": ("rope_rotate", _rotate_interleaved),
@@ -121,6 +138,7 @@ MUTATIONS = {
     "no_inverse_rotation": ("head_backward", _make_backward("no_inverse_rotation")),
     "v_rotated": ("head_forward", _forward_rotates_v),
     "k_unrotated": ("head_forward", _forward_k_unrotated),
+    "decode_position_off_by_one": ("attn_decode", _decode_position_off_by_one),
 }
 
 

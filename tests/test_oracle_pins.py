@@ -398,3 +398,44 @@ def test_oracle_regression_fixture():
         for name, g in zip(["o", "lse", "dq", "dk", "dv"], got):
             np.testing.assert_allclose(g, np.array(case[name]), rtol=1e-12, atol=1e-12,
                                        err_msg=f"{case['name']}:{name}")
+
+
+@pytest.mark.parametrize("rd,D,t", [(16, 64, 0), (24, 96, 5), (128, 128, 40), (0, 64, 17)])
+def test_decode_step_is_the_last_causal_row(rd, D, t):
+    """A decoding step over a cache of t rotated keys equals row t of causal
+    attention over the t + 1 tokens (computed by the full-matrix path, which is
+    itself pinned to torch's float64 SDPA)."""
+    rng = np.random.default_rng(500 + t)
+    q, k, v = (_rand(rng, t + 1, D) for _ in range(3))
+    k_cache = orc.rope_rotate(k[:t], np.arange(t), rd, 10000.0)
+    o, lse, k_rot = orc.attn_decode(q[t], k[t], v[t], k_cache, v[:t], rotary_dim=rd)
+    of, lf = orc.attn_fwd(q[None, None], k[None, None], v[None, None], rotary_dim=rd)
+    np.testing.assert_allclose(o, of[0, 0, t], rtol=0, atol=1e-12)
+    assert abs(lse - lf[0, 0, t]) < 1e-12
+
+
+def test_decode_first_token_returns_v():
+    """Position 0 leaves q and k unrotated; with one token the output is v and
+    the logsumexp is the single score scale * q . k."""
+    rng = np.random.default_rng(510)
+    q, k, v = (_rand(rng, 96) for _ in range(3))
+    o, lse, k_rot = orc.attn_decode(q, k, v, np.zeros((0, 96)), np.zeros((0, 96)),
+                                    rotary_dim=24)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    assert abs(lse - float(q @ k) / math.sqrt(96)) < 1e-12
+    np.testing.assert_allclose(k_rot, k, rtol=0, atol=1e-15)
+
+
+def test_decode_appended_key_is_rotated_at_its_position():
+    """The appended key is k times exp(i t w_p) in the complex pair form."""
+    rng = np.random.default_rng(511)
+    rd, D, t = 24, 96, 33
+    q, k, v = (_rand(rng, D) for _ in range(3))
+    k_cache, v_cache = _rand(rng, t, D), _rand(rng, t, D)
+    _, _, k_rot = orc.attn_decode(q, k, v, k_cache, v_cache, rotary_dim=rd)
+    h = rd // 2
+    w = np.exp(-(2.0 * np.arange(h) / rd) * math.log(10000.0))
+    z = (k[:h] + 1j * k[h:rd]) * np.exp(1j * t * w)
+    np.testing.assert_allclose(k_rot[:h], z.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k_rot[h:rd], z.imag, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(k_rot[rd:], k[rd:])
