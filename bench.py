@@ -14,8 +14,9 @@ value = algorithmic fwd+bwd FLOP per step / time per step, in TFLOP/s:
 
 The JSON line also carries the roofline of the dominant kernel (timed live via
 per-phase HIP events recorded by the library on the launch stream), the forward
-efficiency at S=2048, D=128, and the CPU oracle timed on a bounded sample of
-the same workload on this host's cores.
+efficiency at S=2048, D=128, the decoding step's HBM rate (one new token per
+sequence against a 2048-row cache), and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
 """
 
 from __future__ import annotations
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-fwd-target", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a plain 1 GiB device copy (scale for traffic counters)")
     return ap.parse_args()
@@ -169,6 +171,43 @@ def fwd_target(args, torch, np, neox, W):
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "attn_kernel_us": round(ms_attn * 1e3, 2),
             "attn_kernel_frac": round(tf_attn / PEAK_BF16_TFLOPS, 4)}
+
+
+def decode(args, torch, np, neox, W):
+    """One decoding step (new token against a full 2048-row cache, 20B head
+    layout), timed back to back.  Two copies of the cache alternate so that the
+    step cannot be served from the last-level cache (each copy is larger than
+    it); the rate counts the algorithmic HBM bytes of one step."""
+    wl = W.DECODE_WORKLOADS[W.DECODE_BENCH_WORKLOAD]
+    inp = W.generate_decode(wl)
+    dt = wl.dtype
+    q, k, v = (dev_tensor(torch, np, getattr(inp, n), dt) for n in ("q", "k", "v"))
+    caches = [(dev_tensor(torch, np, inp.k_cache, dt), dev_tensor(torch, np, inp.v_cache, dt))
+              for _ in range(2)]
+    lens = torch.from_numpy(inp.lens.copy()).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(neox.neox_rope_attn_decode_workspace_size(wl.B, wl.H, wl.D, wl.cap),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda i: neox.neox_rope_attn_decode(  # noqa: E731
+        q, k, v, caches[i & 1][0], caches[i & 1][1], lens, o, lse, wl.rotary_dim, wl.rope_base,
+        wl.softmax_scale, workspace=ws)
+    for i in range(max(args.warmup, 2)):
+        call(i)
+    n = max(4 * args.steps, 100)
+    start, end = make_events(torch, 2)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(n):
+        call(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    nbytes = W.decode_bytes(wl, inp.lens)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "rotary_dim": wl.rotary_dim,
+            "cache_rows": wl.cap, "position": int(inp.lens.max()), "us_per_call": round(ms * 1e3, 2),
+            "bytes": nbytes, "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline(args, np, W, wl, inp):
@@ -303,6 +342,8 @@ def main():
     }
     if not args.no_fwd_target:
         out["fwd_target"] = fwd_target(args, torch, np, neox, W)
+    if not args.no_decode:
+        out["decode"] = decode(args, torch, np, neox, W)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, np, W, wl, inp)
     print(json.dumps(out), flush=True)

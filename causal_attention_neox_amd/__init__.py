@@ -25,6 +25,7 @@ __all__ = [
     "NeoxError", "neox_status_str", "neox_rope_attn_fwd", "neox_rope_attn_bwd",
     "neox_rope_attn_fwd_workspace_size", "neox_rope_attn_bwd_workspace_size",
     "neox_attn_fwd_ex", "neox_attn_bwd_ex",
+    "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode",
     "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
     "NEOX_F32", "NEOX_BF16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
@@ -196,6 +197,29 @@ def neox_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, *, pos: int = NEOX_POS_R
                                       _ptr(workspace), nbytes, _stream(stream))
     del keep
     _check(st, "neox_attn_bwd_ex")
+
+
+def neox_rope_attn_decode_workspace_size(B: int, H: int, D: int, cap: int) -> int:
+    return int(_lib.load().neox_rope_attn_decode_workspace_size(B, H, D, cap))
+
+
+def neox_rope_attn_decode(q, k, v, k_cache, v_cache, cache_lens, o, lse, rotary_dim: int,
+                          rope_base: float = 10000.0, softmax_scale: Optional[float] = None,
+                          workspace=None, stream=None) -> None:
+    """Calls neox_rope_attn_decode: q, k, v, o are [B, H, D]; k_cache, v_cache are
+    [B, H, cap, D] (row cache_lens[b] is written); cache_lens is an int32 device
+    tensor [B]; lse is fp32 [B, H]; ``workspace`` is a uint8 device tensor of at
+    least neox_rope_attn_decode_workspace_size() bytes."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, D] and the caches [B, H, cap, D]")
+    B, H, D = (int(x) for x in q.shape)
+    cap = int(k_cache.shape[2])
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().neox_rope_attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(o),
+        _ptr(lse), B, H, D, cap, int(rotary_dim), float(rope_base), scale, _dtype_code(q),
+        _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "neox_rope_attn_decode")
 
 
 def neox_check_doc_offsets(offsets_host, S: int) -> int:

@@ -64,6 +64,11 @@ SIGNATURES = {
     "neox_attn_bwd_ex": (c_int, [ctypes.POINTER(NeoxAttnArgs), c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "neox_rope_attn_decode_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "neox_rope_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p,
+                                      c_int, c_int, c_int, c_int, c_int, c_float, c_float,
+                                      c_int, c_void_p, c_size_t, c_void_p]),
     "neox_check_doc_offsets": (c_int, [c_void_p, c_int, c_int, c_int]),
     "neox_rope_table_prepare": (c_int, [c_int, c_int, c_float]),
 }

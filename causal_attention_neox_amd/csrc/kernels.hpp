@@ -59,6 +59,29 @@ struct BwdParams {
   int out_f32;     // dq, dk, dv stored as fp32
 };
 
+// One decoding step: the new token of every (batch, head) against its cache.
+struct DecodeParams {
+  int B, H, D, cap;       // cache rows hold positions 0 .. cap-1
+  int rd;                 // rotary dims (0 = none)
+  const float2* rope;     // [cap][rd/2] (cos, sin) or null when rd == 0
+  float scale_log2;       // softmax scale * log2(e)
+  int bf16;               // 1: bf16 storage, 0: fp32
+  int nsplit;             // key chunks per (batch, head) = ceil(cap / chunk)
+  const int32_t* lens;    // [B] tokens already cached = position of the new token
+  const void* q;          // [B][H][D] new token, raw
+  const void* k;
+  const void* v;
+  void* k_cache;          // [B][H][cap][D], keys stored rotated
+  void* v_cache;
+  void* o;                // [B][H][D]
+  float* lse;             // [B][H]
+  float* qrot;            // [B][H][D] fp32 workspace
+  float* part;            // [B][H][nsplit * 4][D + 4] fp32 workspace: m, l, 2 unused, o[D] per wave
+};
+
+int decode_chunk_keys();
+hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
+
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
 
 // `ev` is null or 3 events: [0] is recorded by the caller before the call;

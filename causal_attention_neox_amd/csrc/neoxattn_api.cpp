@@ -210,6 +210,16 @@ size_t neox_rope_attn_fwd_workspace_size(int B, int H, int S, int D) {
   return 2 * round256((size_t)rows * (size_t)D * 2u);
 }
 
+size_t neox_rope_attn_decode_workspace_size(int B, int H, int D, int cap) {
+  if (B < 1 || H < 1 || D < 1 || D > 4096 || cap < 1) return 0;
+  const int64_t bh = (int64_t)B * H;
+  if (bh * cap >= kMaxRows) return 0;
+  const int chunk = neox::decode_chunk_keys();
+  const int64_t nsplit = (cap + chunk - 1) / chunk;
+  return round256((size_t)bh * (size_t)D * 4u) +
+         round256((size_t)bh * (size_t)(nsplit * 4) * (size_t)(D + 4) * 4u);
+}
+
 const char* neox_status_str(int status) {
   switch (status) {
     case NEOX_OK: return "ok";
@@ -385,6 +395,61 @@ int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* 
   a.out_dtype = NEOX_OUT_SAME;
   return neox_attn_bwd_ex(&a, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
                           stream);
+}
+
+int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, const int32_t* cache_lens, void* o, float* lse, int B,
+                          int H, int D, int cap, int rotary_dim, float rope_base,
+                          float softmax_scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (B < 1 || H < 1 || D < 1 || cap < 1) return NEOX_E_ARG;
+  if ((int64_t)B * H * cap >= kMaxRows) return NEOX_E_ARG;
+  if (dtype != NEOX_F32 && dtype != NEOX_BF16) return NEOX_E_ARG;
+  if (rotary_dim < 0 || rotary_dim > D || (rotary_dim & 1)) return NEOX_E_ARG;
+  if (rotary_dim > 0 && !finite_pos(rope_base)) return NEOX_E_ARG;
+  if (!finite_pos(softmax_scale)) return NEOX_E_ARG;
+  const void* ptrs[] = {q, k, v, k_cache, v_cache, cache_lens, o, lse};
+  for (const void* ptr : ptrs) {
+    if (!ptr) return NEOX_E_ARG;
+    if (!aligned16(ptr)) return NEOX_E_ALIGN;
+  }
+  if (o == q || o == k || o == v || o == k_cache || o == v_cache) return NEOX_E_ARG;
+  if (D != 64 && D != 96 && D != 128) return NEOX_E_UNSUPPORTED;
+  const size_t need = neox_rope_attn_decode_workspace_size(B, H, D, cap);
+  if (!workspace || workspace_bytes < need) return NEOX_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NEOX_E_ALIGN;
+
+  int dev = 0;
+  int st = check_device(&dev);
+  if (st != NEOX_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const float2* rope = nullptr;
+  if (rotary_dim > 0 && (st = get_rope_table(dev, cap, rotary_dim, rope_base, hs, &rope)) != NEOX_OK)
+    return st;
+
+  neox::DecodeParams p;
+  p.B = B;
+  p.H = H;
+  p.D = D;
+  p.cap = cap;
+  p.rd = rotary_dim;
+  p.rope = rope;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.bf16 = dtype == NEOX_BF16 ? 1 : 0;
+  const int chunk = neox::decode_chunk_keys();
+  p.nsplit = (cap + chunk - 1) / chunk;
+  p.lens = cache_lens;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.o = o;
+  p.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  p.qrot = reinterpret_cast<float*>(ws);
+  p.part = reinterpret_cast<float*>(ws + round256((size_t)B * H * (size_t)D * 4u));
+  return neox::launch_decode(p, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
 }
 
 int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S) {

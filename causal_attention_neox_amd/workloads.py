@@ -211,3 +211,100 @@ def total_pairs(inp: "Inputs") -> int:
     if inp.doc_offsets is None:
         return wl.B * wl.H * allowed_pairs(wl.S, wl.causal)
     return wl.H * sum(allowed_pairs(wl.S, wl.causal, row) for row in inp.doc_offsets)
+
+
+# ---------------------------------------------------------------- decoding
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding step for B sequences: the new token's q, k, v [B, H, D] and
+    key/value caches [B, H, cap, D] holding ``lens[b]`` earlier tokens.
+
+    Sizes follow the GPT-NeoX-20B inference configuration of the
+    FasterTransformer guide ("FasterTransformer GPT-NeoX 推理指南", sections
+    "模型配置" and "采样与解码参数": 64 heads of 96 dims, 24 rotary dims,
+    request batch 8) with the 2048-token context of the model.
+    ``lens``: "full" puts every sequence at position cap - 1 (the whole cache
+    is read); "ragged" draws each row's position uniformly from [0, cap - 1].
+    """
+
+    name: str
+    B: int
+    H: int
+    D: int
+    rotary_dim: int
+    cap: int
+    dtype: str
+    lens: str = "full"
+    rope_base: float = 10000.0
+    seed: int = 20260100
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def with_sizes(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS = {
+    "neox20b_decode_b8_cap2048": DecodeWorkload(
+        "neox20b_decode_b8_cap2048", B=8, H=64, D=96, rotary_dim=24, cap=2048, dtype=BF16,
+        lens="full", seed=20260101),
+    "neox20b_decode_b8_cap2048_ragged": DecodeWorkload(
+        "neox20b_decode_b8_cap2048_ragged", B=8, H=64, D=96, rotary_dim=24, cap=2048,
+        dtype=BF16, lens="ragged", seed=20260102),
+}
+DECODE_BENCH_WORKLOAD = "neox20b_decode_b8_cap2048"
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """Generated decode inputs: ``q, k, v`` [B, H, D] and ``k_cache, v_cache``
+    [B, H, cap, D] as storage values (uint16 bf16 bits or float32), ``lens``
+    int32 [B].  Cache rows hold N(0, 1) draws: any vector is a valid rotated
+    key, so the cache needs no rotation to be generated."""
+
+    wl: DecodeWorkload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    lens: np.ndarray
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if self.wl.dtype == BF16:
+            return bf16_bits_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def generate_decode(wl: DecodeWorkload) -> DecodeInputs:
+    """Seeded decode inputs: ``SeedSequence(seed).spawn(6)`` streams for q, k, v,
+    the key cache, the value cache and the lengths; N(0, 1) draws rounded to the
+    storage type as for ``generate``."""
+    ss = np.random.SeedSequence(wl.seed).spawn(6)
+    tok = (wl.B, wl.H, wl.D)
+    cache = (wl.B, wl.H, wl.cap, wl.D)
+    q, k, v = (_draw(np.random.default_rng(s), tok, 1.0, wl.dtype) for s in ss[:3])
+    kc = _draw(np.random.default_rng(ss[3]), cache, 1.0, wl.dtype)
+    vc = _draw(np.random.default_rng(ss[4]), cache, 1.0, wl.dtype)
+    if wl.lens == "full":
+        lens = np.full(wl.B, wl.cap - 1, dtype=np.int32)
+    elif wl.lens == "ragged":
+        lens = np.random.default_rng(ss[5]).integers(0, wl.cap, size=wl.B).astype(np.int32)
+    else:
+        raise ValueError(f"unknown lens mode {wl.lens!r}")
+    return DecodeInputs(wl, q, k, v, kc, vc, lens)
+
+
+def decode_bytes(wl: DecodeWorkload, lens) -> int:
+    """Algorithmic HBM bytes of one decoding step: every (b, h) reads the t + 1
+    cached key and value rows it attends over (the new row included) once;
+    the new token's q, k, v are read, its key and value written into the
+    cache, and o and the fp32 lse written."""
+    es = 2 if wl.dtype == BF16 else 4
+    rows = sum(int(t) + 1 for t in lens) * wl.H
+    return rows * 2 * wl.D * es + wl.B * wl.H * (6 * wl.D * es + 4)

@@ -197,6 +197,51 @@ int neox_attn_bwd_ex(const neox_attn_args* args, const void* q, const void* k, c
                      void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decoding (one new token per sequence against a key/value cache): the
+ * token-by-token generation mode of the GPT-NeoX decoder ("FasterTransformer
+ * GPT-NeoX 推理指南", section "背景").  The new token sits at position
+ * t = cache_lens[b]; the cache already holds the rotated keys k~_0 .. k~_{t-1}
+ * and the values of the earlier tokens of that sequence.
+ *
+ * Bytes of the decode workspace: an fp32 [B, H, D] rotated query and fp32
+ * partial results of [B, H, 4 * ceil(cap / 256), D + 4], each part rounded up
+ * to 256 bytes.  Returns 0 for invalid sizes (<= 0, D > 4096) or overflow.
+ */
+size_t neox_rope_attn_decode_workspace_size(int B, int H, int D, int cap);
+
+/*
+ * One decoding step for every (batch row, head).  With t = cache_lens[b]:
+ *     q~ = R_t q,  k~ = R_t k         (rotation as above, position t)
+ *     k_cache[b, h, t] = k~,  v_cache[b, h, t] = v       (written)
+ *     s_j = softmax_scale * (q~ . k_cache[b, h, j])      for j = 0 .. t
+ *     lse = log sum_j exp(s_j),  o = sum_j exp(s_j - lse) v_cache[b, h, j]
+ * which is row t of the causal forward over positions 0 .. t.
+ *  q, k, v      device [B, H, D] of `dtype`, contiguous, the new token's raw
+ *               projections (read only).
+ *  k_cache,     device [B, H, cap, D] of `dtype`, contiguous; rows 0 .. t-1
+ *  v_cache      are read, row t is written (keys stored rotated).
+ *  cache_lens   device int32 [B]: tokens already cached per batch row, each in
+ *               [0, cap - 1]; not read by the host.  Values outside are
+ *               clamped into that range by the kernels (undefined results, no
+ *               stray access).  The call does not update them: the caller
+ *               increments them after the step.
+ *  o            device [B, H, D] of `dtype` (written).
+ *  lse          device fp32 [B, H], natural log (written).
+ *  workspace    device memory of at least
+ *               neox_rope_attn_decode_workspace_size(B, H, D, cap) bytes,
+ *               256-byte aligned, owned by the caller, overwritten.
+ * Supported: D in {64, 96, 128}; cap >= 1; B*H*cap < 2^31; 0 <= rotary_dim
+ * <= D, even; pointers 16-byte aligned.  The rotary table covers positions
+ * 0 .. cap - 1 (allocated as described above).  Same status codes as the
+ * other entry points; o and lse must not alias the inputs or the cache.
+ */
+int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, const int32_t* cache_lens, void* o, float* lse,
+                          int B, int H, int D, int cap, int rotary_dim, float rope_base,
+                          float softmax_scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Host-side check of a HOST copy of doc_offsets ([B][n_docs + 1] int32):
  * returns NEOX_OK when every row starts at 0, never decreases and ends at S,
  * NEOX_E_ARG otherwise (or for a NULL pointer / bad sizes).  No device work.

@@ -45,6 +45,7 @@ def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ("neox_rope_attn_fwd", "neox_rope_attn_bwd", "neox_rope_attn_bwd_workspace_size",
               "neox_rope_attn_fwd_workspace_size", "neox_attn_fwd_ex", "neox_attn_bwd_ex",
+              "neox_rope_attn_decode", "neox_rope_attn_decode_workspace_size",
               "neox_status_str"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover the header"
@@ -219,3 +220,44 @@ def test_generated_doc_layout_is_valid(lib):
         lengths = lengths[lengths > 0]
         assert lengths.sum() == wl.S
         assert lengths.min() >= wl.doc_min and lengths.max() <= wl.doc_max
+
+
+def dec(lib, q=A1, k=A2, v=A3, kc=A4, vc=A5, lens=A6, o=A7, lse=A8, B=2, H=4, D=64, cap=300,
+        rd=16, base=1e4, scale=0.125, dtype=BF16, ws=None, wsb=None):
+    need = lib.neox_rope_attn_decode_workspace_size(B, H, D, cap)
+    ws = P(0x100000) if ws is None else ws
+    wsb = need if wsb is None else wsb
+    return lib.neox_rope_attn_decode(q, k, v, kc, vc, lens, o, lse, B, H, D, cap, rd, base,
+                                     scale, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_ARG), (dict(kc=None), E_ARG), (dict(lens=None), E_ARG),
+    (dict(lse=None), E_ARG), (dict(B=0), E_ARG), (dict(cap=0), E_ARG), (dict(D=0), E_ARG),
+    (dict(D=80), E_UNSUP), (dict(rd=15), E_ARG), (dict(rd=66), E_ARG),
+    (dict(base=0.0), E_ARG), (dict(scale=float("inf")), E_ARG), (dict(dtype=3), E_ARG),
+    (dict(o=A1), E_ARG), (dict(o=A4), E_ARG), (dict(vc=P(0x50008)), E_ALIGN),
+    (dict(lens=P(0x60004)), E_ALIGN), (dict(ws=P(0)), E_WS), (dict(wsb=64), E_WS),
+    (dict(ws=P(0x100010)), E_ALIGN), (dict(B=1 << 12, H=1 << 10, cap=1 << 10), E_ARG),
+])
+def test_decode_validation(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_decode_workspace_size(lib):
+    """fp32 rotated query [B, H, D] plus (m, l, o[D]) partials for 4 waves of
+    each 256-key chunk, each part rounded up to 256 bytes."""
+    def r256(n):
+        return ((n + 255) // 256) * 256
+    for (B, H, D, cap) in [(1, 1, 64, 1), (2, 4, 96, 256), (16, 64, 96, 2048), (3, 5, 128, 257)]:
+        nsplit = (cap + 255) // 256
+        expect = r256(B * H * D * 4) + r256(B * H * nsplit * 4 * (D + 4) * 4)
+        assert lib.neox_rope_attn_decode_workspace_size(B, H, D, cap) == expect
+    assert lib.neox_rope_attn_decode_workspace_size(0, 1, 64, 16) == 0
+    assert lib.neox_rope_attn_decode_workspace_size(1, 1, 64, 0) == 0
+    assert lib.neox_rope_attn_decode_workspace_size(1 << 12, 1 << 10, 64, 1 << 10) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present on this host")
+def test_valid_decode_without_gpu_fails_loudly(lib):
+    assert dec(lib) == E_DEV

@@ -1,0 +1,227 @@
+"""GPU parity of the decoding step (neox_rope_attn_decode) against the oracle.
+
+* Step-by-step: a few consecutive tokens are decoded per sequence from caches
+  whose rows start at different positions (one empty, one just below the
+  256-key chunk boundary so that the steps cross it); every step's o and lse
+  and the cache rows the steps write are compared element by element.  The
+  oracle keeps its own cache (the generated rows, then its own rotated keys),
+  so no value of the GPU path feeds it.
+* Full size: the 20B head layout (B=8, H=64, D=96, 24 rotary dims) with a
+  2048-row cache, every sequence at the last position and at ragged positions,
+  launched as the benchmark launches it; every head is compared, the written
+  cache row is checked and every other cache row must be left untouched.
+"""
+
+import numpy as np
+import pytest
+
+from causal_attention_neox_amd import workloads as W
+from oracle import neox_oracle as orc
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def torch():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_attention_neox_amd._lib as L
+    L.load()  # fails loudly when the library is missing
+    return torch
+
+
+def _dev(torch, arr, dtype):
+    if dtype == W.BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def _f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _bits(t):
+    """Storage bits of a device tensor as a numpy array (exact comparisons)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.detach().cpu().view(torch.int16).numpy()
+    return t.detach().cpu().numpy().view(np.int32)
+
+
+def _check(name, got, ref, dtype, label):
+    tol = pu.TOL[dtype]
+    assert np.all(np.isfinite(got)), f"{label} {name}: non-finite values"
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"[decode] {label} {name} max_abs {mx:.2e} mean_abs {mean:.2e}", flush=True)
+    assert mx <= tol["max_abs"], f"{label} {name}: max_abs {mx:.3e}"
+    if name != "lse":
+        assert mean <= tol["mean_abs"], f"{label} {name}: mean_abs {mean:.3e}"
+
+
+def _run(torch, neox, wl, q, k, v, kc, vc, lens, stream=None):
+    B, H, D, cap = wl.B, wl.H, wl.D, wl.cap
+    odt = torch.bfloat16 if wl.dtype == W.BF16 else torch.float32
+    o = torch.empty((B, H, D), dtype=odt, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(neox.neox_rope_attn_decode_workspace_size(B, H, D, cap), dtype=torch.uint8,
+                     device="cuda")
+    neox.neox_rope_attn_decode(q, k, v, kc, vc, lens, o, lse, wl.rotary_dim, wl.rope_base,
+                               wl.softmax_scale, workspace=ws)
+    return o, lse
+
+
+STEP_CASES = [
+    # D, rotary_dim, dtype
+    (64, 16, "bf16"),
+    (96, 24, "bf16"),
+    (128, 128, "bf16"),
+    (128, 40, "bf16"),
+    (64, 0, "bf16"),
+    (96, 6, "bf16"),
+    (64, 64, "f32"),
+    (96, 24, "f32"),
+    (128, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[f"D{c[0]}rd{c[1]}-{c[2]}" for c in STEP_CASES])
+def test_decode_steps_every_element(torch, case):
+    import causal_attention_neox_amd as neox
+    D, rd, dtype = case
+    B, H, cap, T = 3, 2, 300, 10
+    start = np.array([0, 250, 290], dtype=np.int32)  # empty; crosses 256; ends at cap - 1
+    wl = W.DecodeWorkload("steps", B=B, H=H, D=D, rotary_dim=rd, cap=cap, dtype=dtype,
+                          lens="ragged", seed=31 + D + rd)
+    cache = W.generate_decode(wl)
+    toks = W.generate(W.Workload("tokens", B=B, H=H, S=T, D=D, rotary_dim=rd, dtype=dtype,
+                                 backward=False, seed=77 + D + rd))
+    print(f"[decode] steps D={D} rd={rd} {dtype} start={start.tolist()} T={T}", flush=True)
+
+    kc, vc = _dev(torch, cache.k_cache, dtype), _dev(torch, cache.v_cache, dtype)
+    lens = torch.from_numpy(start.copy()).cuda()
+    qd, kd, vd = (_dev(torch, getattr(toks, n), dtype) for n in ("q", "k", "v"))
+    outs = []
+    for s in range(T):
+        o, lse = _run(torch, neox, wl, qd[:, :, s].contiguous(), kd[:, :, s].contiguous(),
+                      vd[:, :, s].contiguous(), kc, vc, lens)
+        outs.append((o.clone(), lse.clone()))
+        lens += 1
+    torch.cuda.synchronize()
+
+    q64, k64, v64 = toks.as_f64("q"), toks.as_f64("k"), toks.as_f64("v")
+    kc64, vc64 = cache.as_f64("k_cache"), cache.as_f64("v_cache")
+    ref_o = np.zeros((T, B, H, D))
+    ref_lse = np.zeros((T, B, H))
+    ref_krows = np.zeros((T, B, H, D))
+    for b in range(B):
+        for h in range(H):
+            keys = list(kc64[b, h, :start[b]])
+            vals = list(vc64[b, h, :start[b]])
+            for s in range(T):
+                o, lse, krot = orc.attn_decode(
+                    q64[b, h, s], k64[b, h, s], v64[b, h, s],
+                    np.array(keys).reshape(-1, D), np.array(vals).reshape(-1, D),
+                    rotary_dim=rd, rope_base=wl.rope_base, softmax_scale=wl.softmax_scale)
+                ref_o[s, b, h], ref_lse[s, b, h], ref_krows[s, b, h] = o, lse, krot
+                keys.append(krot)
+                vals.append(v64[b, h, s])
+    got_o = np.stack([_f64(o) for o, _ in outs])
+    got_lse = np.stack([_f64(l) for _, l in outs])
+    _check("o", got_o, ref_o, dtype, f"D{D} rd{rd} {dtype}")
+    _check("lse", got_lse, ref_lse, dtype, f"D{D} rd{rd} {dtype}")
+
+    # The written cache rows: rotated keys to the bar, values copied exactly.
+    kc_got, vc_bits = _f64(kc), _bits(vc)
+    v_bits = _bits(vd)
+    for b in range(B):
+        rows = np.arange(start[b], start[b] + T)
+        _check("k_cache rows", kc_got[b][:, rows], ref_krows[:, b].transpose(1, 0, 2), dtype,
+               f"D{D} rd{rd} {dtype} b{b}")
+        assert np.array_equal(vc_bits[b][:, rows], v_bits[b]), "value rows must be copied exactly"
+        # rows outside the written range are untouched
+        keep = np.setdiff1d(np.arange(cap), rows)
+        kb0 = cache.k_cache.view(np.int16) if dtype == W.BF16 else cache.k_cache.view(np.int32)
+        assert np.array_equal(_bits(kc)[b][:, keep], kb0[b][:, keep])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(W.DECODE_WORKLOADS))
+def test_decode_full_size_every_head(torch, name):
+    import causal_attention_neox_amd as neox
+    wl = W.DECODE_WORKLOADS[name]
+    inp = W.generate_decode(wl)
+    print(f"[decode] full {name} lens={inp.lens.tolist()}", flush=True)
+    dt = wl.dtype
+    kc, vc = _dev(torch, inp.k_cache, dt), _dev(torch, inp.v_cache, dt)
+    lens = torch.from_numpy(inp.lens.copy()).cuda()
+    q, k, v = (_dev(torch, getattr(inp, n), dt) for n in ("q", "k", "v"))
+    o, lse = _run(torch, neox, wl, q, k, v, kc, vc, lens)
+    torch.cuda.synchronize()
+
+    q64, k64, v64 = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    kc64, vc64 = inp.as_f64("k_cache"), inp.as_f64("v_cache")
+    ref_o = np.zeros((wl.B, wl.H, wl.D))
+    ref_lse = np.zeros((wl.B, wl.H))
+    ref_k = np.zeros((wl.B, wl.H, wl.D))
+    for b in range(wl.B):
+        t = int(inp.lens[b])
+        for h in range(wl.H):
+            ref_o[b, h], ref_lse[b, h], ref_k[b, h] = orc.attn_decode(
+                q64[b, h], k64[b, h], v64[b, h], kc64[b, h, :t], vc64[b, h, :t],
+                rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, softmax_scale=wl.softmax_scale)
+    _check("o", _f64(o), ref_o, dt, name)
+    _check("lse", _f64(lse), ref_lse, dt, name)
+
+    kc_got = _f64(kc)
+    kb, vb = _bits(kc), _bits(vc)
+    kb0 = inp.k_cache.view(np.int16) if dt == W.BF16 else inp.k_cache.view(np.int32)
+    vb0 = inp.v_cache.view(np.int16) if dt == W.BF16 else inp.v_cache.view(np.int32)
+    vnew = inp.v.view(np.int16) if dt == W.BF16 else inp.v.view(np.int32)
+    for b in range(wl.B):
+        t = int(inp.lens[b])
+        _check("k_cache row", kc_got[b, :, t], ref_k[b], dt, f"{name} b{b}")
+        assert np.array_equal(vb[b, :, t], vnew[b])
+        keep = np.r_[0:t, t + 1:wl.cap]
+        assert np.array_equal(kb[b][:, keep], kb0[b][:, keep]), "only row t may change"
+        assert np.array_equal(vb[b][:, keep], vb0[b][:, keep]), "only row t may change"
+
+
+def test_decode_first_token_returns_v(torch):
+    """With an empty cache the only key is the token itself: o equals v
+    exactly and lse is its own scaled score."""
+    import causal_attention_neox_amd as neox
+    wl = W.DecodeWorkload("first", B=4, H=3, D=128, rotary_dim=40, cap=64, dtype=W.BF16,
+                          lens="ragged", seed=5)
+    inp = W.generate_decode(wl)
+    kc, vc = _dev(torch, inp.k_cache, wl.dtype), _dev(torch, inp.v_cache, wl.dtype)
+    lens = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    q, k, v = (_dev(torch, getattr(inp, n), wl.dtype) for n in ("q", "k", "v"))
+    o, lse = _run(torch, neox, wl, q, k, v, kc, vc, lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(o), inp.v.view(np.int16))
+    ref = np.array([[orc.attn_decode(inp.as_f64("q")[b, h], inp.as_f64("k")[b, h],
+                                     inp.as_f64("v")[b, h], np.zeros((0, wl.D)),
+                                     np.zeros((0, wl.D)), rotary_dim=wl.rotary_dim,
+                                     softmax_scale=wl.softmax_scale)[1]
+                     for h in range(wl.H)] for b in range(wl.B)])
+    _check("lse", _f64(lse), ref, wl.dtype, "first token")
+
+
+def test_decode_is_deterministic(torch):
+    import causal_attention_neox_amd as neox
+    wl = W.DECODE_WORKLOADS["neox20b_decode_b8_cap2048_ragged"]
+    inp = W.generate_decode(wl)
+    res = []
+    for _ in range(2):
+        kc, vc = _dev(torch, inp.k_cache, wl.dtype), _dev(torch, inp.v_cache, wl.dtype)
+        lens = torch.from_numpy(inp.lens.copy()).cuda()
+        q, k, v = (_dev(torch, getattr(inp, n), wl.dtype) for n in ("q", "k", "v"))
+        o, lse = _run(torch, neox, wl, q, k, v, kc, vc, lens)
+        torch.cuda.synchronize()
+        res.append((_bits(o), lse.cpu().numpy().copy(), _bits(kc)))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][2], res[1][2])
