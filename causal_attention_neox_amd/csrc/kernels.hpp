@@ -66,7 +66,8 @@ struct DecodeParams {
   const float2* rope;     // [cap][rd/2] (cos, sin) or null when rd == 0
   float scale_log2;       // softmax scale * log2(e)
   int bf16;               // 1: bf16 storage, 0: fp32
-  int nsplit;             // key chunks per (batch, head) = ceil(cap / chunk)
+  int chunk;              // cache rows per split workgroup (a multiple of decode_tile_rows())
+  int nsplit;             // chunks per (batch, head) = ceil(cap / chunk)
   const int32_t* lens;    // [B] tokens already cached = position of the new token
   const void* q;          // [B][H][D] new token, raw
   const void* k;
@@ -75,11 +76,12 @@ struct DecodeParams {
   void* v_cache;
   void* o;                // [B][H][D]
   float* lse;             // [B][H]
-  float* qrot;            // [B][H][D] fp32 workspace
-  float* part;            // [B][H][nsplit * 4][D + 4] fp32 workspace: m, l, 2 unused, o[D] per wave
+  float* part;            // [B][H][nsplit][D + 4] fp32 workspace: m, l, 2 unused, o[D] per chunk
+                          // (unused when nsplit == 1)
 };
 
-int decode_chunk_keys();
+int decode_tile_rows();
+void decode_plan(int BH, int cap, int* chunk, int* nsplit);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);

@@ -214,10 +214,9 @@ size_t neox_rope_attn_decode_workspace_size(int B, int H, int D, int cap) {
   if (B < 1 || H < 1 || D < 1 || D > 4096 || cap < 1) return 0;
   const int64_t bh = (int64_t)B * H;
   if (bh * cap >= kMaxRows) return 0;
-  const int chunk = neox::decode_chunk_keys();
-  const int64_t nsplit = (cap + chunk - 1) / chunk;
-  return round256((size_t)bh * (size_t)D * 4u) +
-         round256((size_t)bh * (size_t)(nsplit * 4) * (size_t)(D + 4) * 4u);
+  const int tile = neox::decode_tile_rows();  // the smallest chunk
+  const int64_t nsplit = (cap + tile - 1) / tile;
+  return round256((size_t)bh * (size_t)nsplit * (size_t)(D + 4) * 4u);
 }
 
 const char* neox_status_str(int status) {
@@ -436,8 +435,7 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   p.rope = rope;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.bf16 = dtype == NEOX_BF16 ? 1 : 0;
-  const int chunk = neox::decode_chunk_keys();
-  p.nsplit = (cap + chunk - 1) / chunk;
+  neox::decode_plan(B * H, cap, &p.chunk, &p.nsplit);
   p.lens = cache_lens;
   p.q = q;
   p.k = k;
@@ -446,9 +444,7 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   p.v_cache = v_cache;
   p.o = o;
   p.lse = lse;
-  char* ws = static_cast<char*>(workspace);
-  p.qrot = reinterpret_cast<float*>(ws);
-  p.part = reinterpret_cast<float*>(ws + round256((size_t)B * H * (size_t)D * 4u));
+  p.part = static_cast<float*>(workspace);
   return neox::launch_decode(p, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
 }
 

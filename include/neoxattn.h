@@ -203,9 +203,9 @@ int neox_attn_bwd_ex(const neox_attn_args* args, const void* q, const void* k, c
  * t = cache_lens[b]; the cache already holds the rotated keys k~_0 .. k~_{t-1}
  * and the values of the earlier tokens of that sequence.
  *
- * Bytes of the decode workspace: an fp32 [B, H, D] rotated query and fp32
- * partial results of [B, H, 4 * ceil(cap / 256), D + 4], each part rounded up
- * to 256 bytes.  Returns 0 for invalid sizes (<= 0, D > 4096) or overflow.
+ * Bytes of the decode workspace: fp32 partial results (running max, sum and
+ * weighted value sum) of [B, H, ceil(cap / 256), D + 4], rounded up to 256
+ * bytes.  Returns 0 for invalid sizes (<= 0, D > 4096) or overflow.
  */
 size_t neox_rope_attn_decode_workspace_size(int B, int H, int D, int cap);
 

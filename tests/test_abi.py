@@ -245,13 +245,13 @@ def test_decode_validation(lib, kw, status):
 
 
 def test_decode_workspace_size(lib):
-    """fp32 rotated query [B, H, D] plus (m, l, o[D]) partials for 4 waves of
-    each 256-key chunk, each part rounded up to 256 bytes."""
+    """(m, l, o[D]) fp32 partials, 16-byte aligned records, one per 256-row
+    chunk of the cache, rounded up to 256 bytes."""
     def r256(n):
         return ((n + 255) // 256) * 256
     for (B, H, D, cap) in [(1, 1, 64, 1), (2, 4, 96, 256), (16, 64, 96, 2048), (3, 5, 128, 257)]:
         nsplit = (cap + 255) // 256
-        expect = r256(B * H * D * 4) + r256(B * H * nsplit * 4 * (D + 4) * 4)
+        expect = r256(B * H * nsplit * (D + 4) * 4)
         assert lib.neox_rope_attn_decode_workspace_size(B, H, D, cap) == expect
     assert lib.neox_rope_attn_decode_workspace_size(0, 1, 64, 16) == 0
     assert lib.neox_rope_attn_decode_workspace_size(1, 1, 64, 0) == 0
