@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-fwd-target", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="finish with a plain 1 GiB device copy (scale for traffic counters)")
+                    help="finish with kernels of known traffic (scale for traffic counters)")
     return ap.parse_args()
 
 
@@ -207,7 +207,8 @@ def decode(args, torch, np, neox, W):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "rotary_dim": wl.rotary_dim,
             "cache_rows": wl.cap, "position": int(inp.lens.max()), "us_per_call": round(ms * 1e3, 2),
-            "bytes": nbytes, "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+            "bytes": nbytes, "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("decode", wl.name)}
 
 
 def cpu_baseline(args, np, W, wl, inp):
@@ -348,9 +349,12 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, np, W, wl, inp)
     print(json.dumps(out), flush=True)
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # Known traffic for scaling the HBM byte counters: an elementwise kernel
+        # over the whole chip (1 GiB read, 1 GiB written) and the runtime's copy.
+        src = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)  # reads and writes exactly 1 GiB
+        torch.neg(src, out=dst)
+        dst.copy_(src)
         torch.cuda.synchronize()
 
 
