@@ -38,7 +38,10 @@ notes of this repository):
   R5  ALiBi slope of head h (0-based) is 2^(-8 (h+1) / H);
   R6  allowed(i, j) <=> (not causal or j <= i) and doc(i) == doc(j); the
       diagonal is allowed, so every row has at least one key;
-  R7  lse is the natural-log logsumexp of the allowed scores of a row.
+  R7  lse is the natural-log logsumexp of the allowed scores of a row;
+  R8  with packed documents the rotary positions are 0..S-1 along the batch row,
+      or, when asked for (``rope_doc_positions``), the token's offset inside its
+      document, so that each packed document is rotated as if it stood alone.
 
 Pins (tests that fix this oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``: torch's float64 scaled_dot_product_attention and
@@ -127,6 +130,17 @@ def doc_index(offsets_row: Optional[np.ndarray], S: int) -> np.ndarray:
     return np.searchsorted(off, t, side="right") - 1
 
 
+def rope_positions(S: int, offsets_row: Optional[np.ndarray] = None,
+                   per_document: bool = False) -> np.ndarray:
+    """Rotary position of each token of a batch row (R3, R8): t, or with
+    ``per_document`` the offset t - offsets[doc(t)] of t inside its document."""
+    t = np.arange(S)
+    if not per_document or offsets_row is None:
+        return t
+    off = np.asarray(offsets_row, dtype=np.int64)
+    return t - off[doc_index(offsets_row, S)]
+
+
 def allowed_mask(S: int, causal: bool, offsets_row: Optional[np.ndarray]) -> np.ndarray:
     """Boolean [S, S]: allowed[i, j] (R6)."""
     i = np.arange(S)[:, None]
@@ -166,10 +180,11 @@ def _head_probs(qr, kr, scale, bias, allowed):
 
 
 def head_forward(q, k, v, *, rotary_dim, rope_base, causal, scale, slope=None,
-                 offsets_row=None):
-    """o [S, D] and lse [S] of one head."""
+                 offsets_row=None, positions=None):
+    """o [S, D] and lse [S] of one head; ``positions`` are the rotary positions
+    (default 0..S-1)."""
     S = q.shape[0]
-    pos = np.arange(S)
+    pos = np.arange(S) if positions is None else np.asarray(positions)
     qr = rope_rotate(q, pos, rotary_dim, rope_base)
     kr = rope_rotate(k, pos, rotary_dim, rope_base)
     bias = alibi_bias(S, slope) if slope is not None else None
@@ -179,7 +194,7 @@ def head_forward(q, k, v, *, rotary_dim, rope_base, causal, scale, slope=None,
 
 
 def head_backward(q, k, v, dout, *, rotary_dim, rope_base, causal, scale, slope=None,
-                  offsets_row=None):
+                  offsets_row=None, positions=None):
     """(o, lse, dq, dk, dv) of one head, by differentiating the definition.
 
     dv_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  Delta_i = dO_i . o_i;
@@ -188,7 +203,7 @@ def head_backward(q, k, v, dout, *, rotary_dim, rope_base, causal, scale, slope=
     The bias does not depend on q, k, v, so it adds no gradient term.
     """
     S = q.shape[0]
-    pos = np.arange(S)
+    pos = np.arange(S) if positions is None else np.asarray(positions)
     qr = rope_rotate(q, pos, rotary_dim, rope_base)
     kr = rope_rotate(k, pos, rotary_dim, rope_base)
     bias = alibi_bias(S, slope) if slope is not None else None
@@ -226,10 +241,12 @@ def _slopes(H, alibi):
 def attn_fwd(q, k, v, *, rotary_dim: int, rope_base: float = 10000.0, causal: bool = True,
              softmax_scale: Optional[float] = None, alibi=False,
              doc_offsets: Optional[np.ndarray] = None,
-             heads: Optional[Sequence[Tuple[int, int]]] = None):
+             heads: Optional[Sequence[Tuple[int, int]]] = None,
+             rope_doc_positions: bool = False):
     """Forward of attention over [B, H, S, D] float64 inputs.
 
     ``alibi`` is False, True (slopes by R5) or an explicit [H] slope array.
+    ``rope_doc_positions`` restarts the rotary positions at each document (R8).
     ``heads`` restricts the work to a list of (b, h); the results are then
     stacked in that order as o [n, S, D] and lse [n, S].  Heads are independent,
     so a restricted run gives exactly the full run's values for those heads.
@@ -241,10 +258,11 @@ def attn_fwd(q, k, v, *, rotary_dim: int, rope_base: float = 10000.0, causal: bo
     o = np.empty((len(hl), S, D))
     lse = np.empty((len(hl), S))
     for n, (b, h) in enumerate(hl):
+        offs = None if doc_offsets is None else doc_offsets[b]
         o[n], lse[n] = head_forward(
             q[b, h], k[b, h], v[b, h], rotary_dim=rotary_dim, rope_base=rope_base,
             causal=causal, scale=scale, slope=None if slopes is None else slopes[h],
-            offsets_row=None if doc_offsets is None else doc_offsets[b])
+            offsets_row=offs, positions=rope_positions(S, offs, rope_doc_positions))
     if heads is None:
         return o.reshape(B, H, S, D), lse.reshape(B, H, S)
     return o, lse
@@ -253,7 +271,8 @@ def attn_fwd(q, k, v, *, rotary_dim: int, rope_base: float = 10000.0, causal: bo
 def attn_bwd(q, k, v, dout, *, rotary_dim: int, rope_base: float = 10000.0,
              causal: bool = True, softmax_scale: Optional[float] = None, alibi=False,
              doc_offsets: Optional[np.ndarray] = None,
-             heads: Optional[Sequence[Tuple[int, int]]] = None):
+             heads: Optional[Sequence[Tuple[int, int]]] = None,
+             rope_doc_positions: bool = False):
     """(o, lse, dq, dk, dv) over [B, H, S, D] float64 inputs; see attn_fwd."""
     B, H, S, D = q.shape
     scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -262,11 +281,12 @@ def attn_bwd(q, k, v, dout, *, rotary_dim: int, rope_base: float = 10000.0,
     out = [np.empty((len(hl), S, D)), np.empty((len(hl), S)), np.empty((len(hl), S, D)),
            np.empty((len(hl), S, D)), np.empty((len(hl), S, D))]
     for n, (b, h) in enumerate(hl):
+        offs = None if doc_offsets is None else doc_offsets[b]
         res = head_backward(
             q[b, h], k[b, h], v[b, h], dout[b, h], rotary_dim=rotary_dim,
             rope_base=rope_base, causal=causal, scale=scale,
-            slope=None if slopes is None else slopes[h],
-            offsets_row=None if doc_offsets is None else doc_offsets[b])
+            slope=None if slopes is None else slopes[h], offsets_row=offs,
+            positions=rope_positions(S, offs, rope_doc_positions))
         for dst, r in zip(out, res):
             dst[n] = r
     if heads is None:

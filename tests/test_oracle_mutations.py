@@ -13,7 +13,7 @@ from tests import test_oracle_pins as pins
 
 ORIG = {n: getattr(orc, n) for n in
         ("rope_rotate", "rope_inv_freq", "allowed_mask", "alibi_bias", "_head_probs",
-         "head_backward", "head_forward", "alibi_slopes", "attn_decode")}
+         "head_backward", "head_forward", "alibi_slopes", "attn_decode", "rope_positions")}
 
 
 def _rotate_sign_flipped(x, positions, rotary_dim, base, inverse=False):
@@ -67,9 +67,9 @@ def _probs_scale_dropped(qr, kr, scale, bias, allowed):
 
 def _make_backward(variant):
     def head_backward(q, k, v, dout, *, rotary_dim, rope_base, causal, scale, slope=None,
-                      offsets_row=None):
+                      offsets_row=None, positions=None):
         S = q.shape[0]
-        pos = np.arange(S)
+        pos = np.arange(S) if positions is None else positions
         qr = orc.rope_rotate(q, pos, rotary_dim, rope_base)
         kr = orc.rope_rotate(k, pos, rotary_dim, rope_base)
         bias = orc.alibi_bias(S, slope) if slope is not None else None
@@ -89,17 +89,19 @@ def _make_backward(variant):
 
 
 def _forward_rotates_v(q, k, v, *, rotary_dim, rope_base, causal, scale, slope=None,
-                       offsets_row=None):
-    vr = ORIG["rope_rotate"](v, np.arange(q.shape[0]), rotary_dim, rope_base)
+                       offsets_row=None, positions=None):
+    pos = np.arange(q.shape[0]) if positions is None else positions
+    vr = ORIG["rope_rotate"](v, pos, rotary_dim, rope_base)
     return ORIG["head_forward"](q, k, vr, rotary_dim=rotary_dim, rope_base=rope_base,
                                 causal=causal, scale=scale, slope=slope,
-                                offsets_row=offsets_row)
+                                offsets_row=offsets_row, positions=positions)
 
 
 def _forward_k_unrotated(q, k, v, *, rotary_dim, rope_base, causal, scale, slope=None,
-                         offsets_row=None):
+                         offsets_row=None, positions=None):
     S = q.shape[0]
-    qr = orc.rope_rotate(q, np.arange(S), rotary_dim, rope_base)
+    pos = np.arange(S) if positions is None else positions
+    qr = orc.rope_rotate(q, pos, rotary_dim, rope_base)
     bias = orc.alibi_bias(S, slope) if slope is not None else None
     P, lse = orc._head_probs(qr, k, scale, bias, orc.allowed_mask(S, causal, offsets_row))
     return P @ v, lse
@@ -122,6 +124,11 @@ def _decode_position_off_by_one(q, k, v, k_cache, v_cache, *, rotary_dim, rope_b
     return (e / e.sum()) @ vals, m + np.log(e.sum()), kr
 
 
+def _positions_off_by_one_at_documents(S, offsets_row=None, per_document=False):
+    pos = ORIG["rope_positions"](S, offsets_row, per_document)
+    return np.where(pos > 0, pos - 1, pos) if per_document else pos  # slip: start at -1 / 0 twice
+
+
 MUTATIONS = {
     "rotation_sign": ("rope_rotate", _rotate_sign_flipped),
     "rotation_interleaved": ("rope_rotate", _rotate_interleaved),
@@ -139,6 +146,7 @@ MUTATIONS = {
     "v_rotated": ("head_forward", _forward_rotates_v),
     "k_unrotated": ("head_forward", _forward_k_unrotated),
     "decode_position_off_by_one": ("attn_decode", _decode_position_off_by_one),
+    "document_positions_slip": ("rope_positions", _positions_off_by_one_at_documents),
 }
 
 

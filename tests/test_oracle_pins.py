@@ -222,6 +222,43 @@ def test_packed_documents_equal_separate_runs():
                 np.testing.assert_allclose(f[:, :, a:b], p, atol=1e-10)
 
 
+def test_rope_positions_restart_per_document():
+    """Positions inside documents, by hand: [0,3) [3,3) [3,7) [7,10)."""
+    offs = np.array([0, 3, 3, 7, 10])
+    np.testing.assert_array_equal(orc.rope_positions(10, offs, True),
+                                  [0, 1, 2, 0, 1, 2, 3, 0, 1, 2])
+    np.testing.assert_array_equal(orc.rope_positions(10, offs, False), np.arange(10))
+    np.testing.assert_array_equal(orc.rope_positions(10, None, True), np.arange(10))
+
+
+def test_document_positions_equal_separate_runs_and_global_positions():
+    """With positions restarted at each document, every document is rotated as
+    if it stood alone: the packed run equals separate runs (positions from 0),
+    forward and backward.  R_a^T R_b = R_(b-a), so shifting both positions of a
+    pair by the document start changes no score: the global-position run
+    agrees too (to rounding)."""
+    rng = np.random.default_rng(21)
+    S, D = 70, 32
+    offs = np.array([[0, 17, 17, 50, 70]], dtype=np.int32)
+    q, k, v, do = (_rand(rng, 1, 2, S, D) for _ in range(4))
+    for rd in (8, 32):
+        per_doc = orc.attn_bwd(q, k, v, do, rotary_dim=rd, rope_base=50.0, doc_offsets=offs,
+                               rope_doc_positions=True)
+        glob = orc.attn_bwd(q, k, v, do, rotary_dim=rd, rope_base=50.0, doc_offsets=offs)
+        for f, g in zip(per_doc, glob):
+            np.testing.assert_allclose(f, g, atol=1e-10)
+        for a, b in zip(offs[0][:-1], offs[0][1:]):
+            if a == b:
+                continue
+            part = orc.attn_bwd(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], do[:, :, a:b],
+                                rotary_dim=rd, rope_base=50.0)
+            for f, p in zip(per_doc, part):
+                np.testing.assert_allclose(f[:, :, a:b], p, atol=1e-10)
+        o, _ = orc.attn_fwd(q, k, v, rotary_dim=rd, rope_base=50.0, doc_offsets=offs,
+                            rope_doc_positions=True)
+        np.testing.assert_allclose(o, per_doc[0], atol=1e-12)
+
+
 # ---------------------------------------------------------------- library special case
 
 def _torch_reference(q, k, v, do, rd, base, causal, scale, slopes, offs):
