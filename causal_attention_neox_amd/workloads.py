@@ -52,6 +52,12 @@ class Workload:
     doc_max: int = 4096
     amp: float = 1.0
     seed: int = 20260000
+    # With packed documents and RoPE: rotary positions restart at each document
+    # start (each document rotated as if it stood alone).  Scores depend only on
+    # position differences inside a document, so the attention results equal
+    # those of positions 0..S-1 along the row; the flag tells the oracle which
+    # reading to compute.
+    rope_doc_positions: bool = False
 
     @property
     def softmax_scale(self) -> float:
@@ -61,9 +67,10 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads the library is measured and checked on, plus the S=2048,
-# D=128 shape used for the forward-efficiency figure.  Seeds are 20260000 + the
-# workload's index (1-based for the five, 6 for the D=128 shape).
+# The five workloads the library is measured and checked on, the S=2048, D=128
+# shape used for the forward-efficiency figure and the packed documents with
+# RoPE.  Seeds are 20260000 + the workload's index (1-based for the five, 6 for
+# the D=128 shape, 7 for RoPE with documents).
 WORKLOADS = {
     "fp32_s128_d64": Workload(
         "fp32_s128_d64", B=1, H=2, S=128, D=64, rotary_dim=64, dtype=F32,
@@ -83,6 +90,12 @@ WORKLOADS = {
     "rope_s2048_d128": Workload(
         "rope_s2048_d128", B=4, H=32, S=2048, D=128, rotary_dim=128,
         dtype=BF16, seed=20260006),
+    # The packed-document layout of the ALiBi workload with RoPE instead (a
+    # quarter of the head dim rotated, the 20B model's 24 of 96), positions
+    # restarting at each document.
+    "rope_docs_s4096_d128": Workload(
+        "rope_docs_s4096_d128", B=4, H=32, S=4096, D=128, rotary_dim=32,
+        dtype=BF16, packed_docs=True, rope_doc_positions=True, seed=20260007),
 }
 
 # Workload whose fwd+bwd throughput is the headline figure: the 2048-token

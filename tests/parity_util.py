@@ -83,7 +83,7 @@ def oracle_heads(inp: Inputs, heads, backward: bool = True):
     res = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
     for n, (b, h) in enumerate(heads):
         kw = dict(rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
-                  softmax_scale=wl.softmax_scale,
+                  softmax_scale=wl.softmax_scale, rope_doc_positions=wl.rope_doc_positions,
                   alibi=False if slopes_all is None else slopes_all[h:h + 1],
                   doc_offsets=None if inp.doc_offsets is None else inp.doc_offsets[b:b + 1])
         if backward:

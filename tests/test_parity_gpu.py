@@ -8,6 +8,8 @@ launches them and are compared on sampled heads, which the oracle computes
 exactly (heads are independent).
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -93,6 +95,13 @@ def test_packed_documents_every_element(case):
     gpu = pu.run_library(inp, backward=True)
     ref = pu.oracle_heads(inp, heads)
     pu.compare(gpu, ref, heads, "bf16", label=f"docs S={S} D={D} alibi={alibi} causal={causal}")
+    if not alibi:
+        # Rotary positions restarting at each document give the same attention
+        # (scores depend on position differences only): the same outputs meet
+        # the bar against that reading too.
+        inp.wl = dataclasses.replace(wl, rope_doc_positions=True)
+        ref = pu.oracle_heads(inp, heads)
+        pu.compare(gpu, ref, heads, "bf16", label=f"docs S={S} D={D} document positions")
 
 
 def test_fp32_workload_full():
@@ -105,11 +114,11 @@ def test_fp32_workload_full():
 
 
 FULL = ["bf16_s2048_d64_rd16", "neox20b_s2048_h64_d96_rd24", "alibi_docs_s4096_d128",
-        "rope_s2048_d128", "long_s16384_d128"]
+        "rope_s2048_d128", "long_s16384_d128", "rope_docs_s4096_d128"]
 # Workloads whose gradients reach |x| >= 4, where bf16 storage alone costs up to
 # 2^-6 = 0.0156 of the 0.02 max-abs budget: checked in the library's fp32-output
 # mode (NEOX_OUT_F32), which is what such callers use.
-FULL_OUT_F32 = {"alibi_docs_s4096_d128"}
+FULL_OUT_F32 = {"alibi_docs_s4096_d128", "rope_docs_s4096_d128"}
 
 
 @pytest.mark.timeout(900)
@@ -204,6 +213,39 @@ def test_strided_packed_qkv_matches_contiguous(gpu):
     assert torch.equal(grads[1].view(torch.int16), ref["dk"].view(torch.int16))
     assert torch.equal(grads[2].view(torch.int16), ref["dv"].view(torch.int16))
     assert torch.equal(grads[0].view(torch.int16), ref["dq"].view(torch.int16))  # deterministic
+
+
+def test_neox_fused_qkv_layout_through_strides(gpu):
+    """q, k, v read in place from NeoX's fused projection output, per token
+    [heads, 3, head_dim] (the FT guide's QKV weight layout [hidden, 3, heads,
+    head] is the converted form of HF's [hidden, heads, 3, head]): a
+    [B, S, H, 3, D] buffer, head stride 3 D, sequence stride 3 H D.  Gradients
+    are written into the same interleaved layout."""
+    torch = gpu
+    import causal_attention_neox_amd as neox
+    wl = pu.small_workload(2, 3, 257, 96, 24, seed=17)
+    inp = generate(wl)
+    q, k, v, do = (pu.to_device(inp, n) for n in ("q", "k", "v", "dout"))
+    B, H, S, D = q.shape
+    packed = torch.stack([q, k, v], dim=0).permute(1, 3, 2, 0, 4).contiguous()  # [B,S,H,3,D]
+    qs, ks, vs = (packed[:, :, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert qs.stride() == (S * H * 3 * D, 3 * D, H * 3 * D, 1)
+    ref = pu.run_library(inp, backward=True)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                      device="cuda")
+    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=24, workspace=fws)
+    gpacked = torch.full_like(packed, float("nan"))
+    gq, gk, gv = (gpacked[:, :, :, i].permute(0, 2, 1, 3) for i in range(3))
+    ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                     device="cuda")
+    neox.neox_attn_bwd_ex(qs, ks, vs, o, do, lse, gq, gk, gv, rotary_dim=24, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref["o"].view(torch.int16))
+    assert torch.equal(lse, ref["lse"])
+    for g, name in ((gq, "dq"), (gk, "dk"), (gv, "dv")):
+        assert torch.equal(g.contiguous().view(torch.int16), ref[name].view(torch.int16)), name
 
 
 def test_fp32_outputs_option(gpu):
