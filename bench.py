@@ -14,7 +14,7 @@ value = algorithmic fwd+bwd FLOP per step / time per step, in TFLOP/s:
 
 The JSON line also carries the roofline of the dominant kernel (timed live via
 per-phase HIP events recorded by the library on the launch stream), the forward
-efficiency at S=2048, D=128, the decoding step's HBM rate (one new token per
+efficiency at S=2048, D=128, the same step with fp16 storage, the decoding step's HBM rate (one new token per
 sequence against a 2048-row cache), and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 """
@@ -32,7 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "causal RoPE-attention fwd+bwd TFLOP/s at S=2048 (1 GPU) + % of bf16 MFMA peak"
-# Dense bf16 MFMA peak of MI355X: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
+# Dense bf16 (and fp16) MFMA peak of MI355X: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 
@@ -48,14 +48,16 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-fwd-target", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with kernels of known traffic (scale for traffic counters)")
     return ap.parse_args()
 
 
 def dev_tensor(torch, np, arr, dtype):
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype in ("bf16", "f16"):
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(tdt).cuda()
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
@@ -171,6 +173,21 @@ def fwd_target(args, torch, np, neox, W):
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "attn_kernel_us": round(ms_attn * 1e3, 2),
             "attn_kernel_frac": round(tf_attn / PEAK_BF16_TFLOPS, 4)}
+
+
+def fp16_step(args, torch, np, neox, W, wl):
+    """The same fwd+bwd step with fp16 storage (the precision FasterTransformer
+    runs GPT-NeoX in), timed the same way."""
+    import dataclasses
+    wl16 = dataclasses.replace(wl, dtype="f16")
+    inp16 = W.generate(wl16)
+    total_ms, kms = run_gpu(args, torch, np, neox, W, wl16, inp16)
+    ms = total_ms / args.steps
+    pairs = W.total_pairs(inp16)
+    tf = 14 * wl.D * pairs / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "dtype": "f16", "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+            "frac_of_f16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kms.items()}}
 
 
 def decode(args, torch, np, neox, W):
@@ -343,6 +360,8 @@ def main():
     }
     if not args.no_fwd_target:
         out["fwd_target"] = fwd_target(args, torch, np, neox, W)
+    if not args.no_fp16:
+        out["fp16"] = fp16_step(args, torch, np, neox, W, wl)
     if not args.no_decode:
         out["decode"] = decode(args, torch, np, neox, W)
     if not args.no_cpu_baseline:

@@ -18,7 +18,7 @@ import math
 from typing import Optional
 
 from . import _lib
-from ._lib import (NEOX_BF16, NEOX_F32, NEOX_OUT_F32, NEOX_OUT_SAME, NEOX_POS_ALIBI,
+from ._lib import (NEOX_BF16, NEOX_F16, NEOX_F32, NEOX_OUT_F32, NEOX_OUT_SAME, NEOX_POS_ALIBI,
                    NEOX_POS_NONE, NEOX_POS_ROPE)
 
 __all__ = [
@@ -27,7 +27,7 @@ __all__ = [
     "neox_attn_fwd_ex", "neox_attn_bwd_ex",
     "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode",
     "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
-    "NEOX_F32", "NEOX_BF16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
+    "NEOX_F32", "NEOX_BF16", "NEOX_F16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
 ]
 
@@ -53,9 +53,12 @@ def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
         return NEOX_BF16
+    if t.dtype == torch.float16:
+        return NEOX_F16
     if t.dtype == torch.float32:
         return NEOX_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16, torch.float16 or "
+                    "torch.float32")
 
 
 def _shape(q):

@@ -23,7 +23,7 @@ class NeoxAttentionFn(torch.autograd.Function):
         kw = dict(pos=pos, rotary_dim=rotary_dim, rope_base=rope_base, alibi_slopes=alibi_slopes,
                   causal=causal, softmax_scale=softmax_scale, doc_offsets=doc_offsets)
         ws = None
-        if rotary_dim > 0 and not alibi and q.dtype == torch.bfloat16:
+        if rotary_dim > 0 and not alibi and q.dtype in (torch.bfloat16, torch.float16):
             ws = torch.empty(neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                              device=q.device)
         neox_attn_fwd_ex(q, k, v, o, lse, out_f32=out_f32, workspace=ws, **kw)

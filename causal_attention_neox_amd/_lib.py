@@ -23,6 +23,7 @@ NEOX_E_ALLOC = -7
 
 NEOX_F32 = 0
 NEOX_BF16 = 1
+NEOX_F16 = 2
 NEOX_POS_NONE = 0
 NEOX_POS_ROPE = 1
 NEOX_POS_ALIBI = 2

@@ -1,4 +1,5 @@
-// Backward attention on gfx950, bf16 storage, bf16 MFMA with fp32 accumulation.
+// Backward attention on gfx950, 16-bit storage (bf16; bwd_f16.hip compiles this
+// file again for IEEE half), MFMA on that type with fp32 accumulation.
 //
 // Recompute-based backward of the tiled exact attention (GPT-NeoX trains with
 // the FlashAttention-2 form, "GPT-NeoX 开源训练框架深度解读", section
@@ -27,6 +28,7 @@
 #include "device_common.hpp"
 
 namespace neox {
+namespace NEOX_ELEM_NS {
 namespace {
 
 constexpr int BNK = 128;  // keys per dK/dV workgroup (4 key groups x 32)
@@ -37,9 +39,9 @@ __device__ __forceinline__ s16x4 tr4(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
-__device__ __forceinline__ bf16x8 tr8(const uint16_t* p, int second) {
+__device__ __forceinline__ elem8 tr8(const uint16_t* p, int second) {
   const s16x4 a = tr4(p), b = tr4(p + second);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(elem8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 __device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_block) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
@@ -109,8 +111,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   float sum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sum = fmaf(bf_lo(ow[e]), bf_lo(gw[e]), sum);
-    sum = fmaf(bf_hi(ow[e]), bf_hi(gw[e]), sum);
+    sum = fmaf(el_lo(ow[e]), el_lo(gw[e]), sum);
+    sum = fmaf(el_hi(ow[e]), el_hi(gw[e]), sum);
   }
 #pragma unroll
   for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
@@ -133,10 +135,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     float xq[8], xk[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      xq[2 * e] = bf_lo(qw[e]);
-      xq[2 * e + 1] = bf_hi(qw[e]);
-      xk[2 * e] = bf_lo(kw[e]);
-      xk[2 * e + 1] = bf_hi(kw[e]);
+      xq[2 * e] = el_lo(qw[e]);
+      xq[2 * e + 1] = el_hi(qw[e]);
+      xk[2 * e] = el_lo(kw[e]);
+      xk[2 * e + 1] = el_hi(kw[e]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         const bool first = d < half;
         const int pd = first ? d + half : d - half;
         const float sn = first ? -cs[e].y : cs[e].y;  // rotate-half: (-x2, x1)
-        xq[e] = fmaf(bf2f(rowbuf[wave][rw][0][pd]), sn, xq[e] * cs[e].x);
-        xk[e] = fmaf(bf2f(rowbuf[wave][rw][1][pd]), sn, xk[e] * cs[e].x);
+        xq[e] = fmaf(el2f(rowbuf[wave][rw][0][pd]), sn, xq[e] * cs[e].x);
+        xk[e] = fmaf(el2f(rowbuf[wave][rw][1][pd]), sn, xk[e] * cs[e].x);
       }
     }
     qw = u32x4{pack2(xq[0], xq[1]), pack2(xq[2], xq[3]), pack2(xq[4], xq[5]), pack2(xq[6], xq[7])};
@@ -302,14 +304,14 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     if constexpr (!kRegKV) load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, lds + L::VT + 512 * blk);
   }
   fetch_q(qt_lo, lds + L::Q0, fl);
-  bf16x8 kreg[kRegKV ? D / 16 : 1], vreg[kRegKV ? D / 16 : 1];
+  elem8 kreg[kRegKV ? D / 16 : 1], vreg[kRegKV ? D / 16 : 1];
   if constexpr (kRegKV) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      vreg[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      vreg[c] = __builtin_bit_cast(elem8, u32x4{0u, 0u, 0u, 0u});
       if (j < S)
         vreg[c] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(vb + (int64_t)j * p.sv.s + 16 * c + 8 * hh));
+            elem8, *reinterpret_cast<const u32x4*>(vb + (int64_t)j * p.sv.s + 16 * c + 8 * hh));
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     // Operands of dims step c: Q~ and dO rows (and K~ / V rows from LDS),
     // read one step ahead of the MFMAs that use them.
     struct Ops {
-      bf16x8 q, g, k, v;
+      elem8 q, g, k, v;
     };
     auto ops = [&](int c) {
       const int off = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       pds(std::false_type{});
     }
 
-    bf16x8 pb[2], sb[2];
+    elem8 pb[2], sb[2];
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       float pv[8], sv[8];
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     auto tops = [&](int g) {
       const int off = taddr[0][g % NB] + 16 * (g / NB) * D;
       const int second = taddr[1][g % NB] - taddr[0][g % NB];
-      return Ops{tr8(Qt + off, second), tr8(Gt + off, second), bf16x8{}, bf16x8{}};
+      return Ops{tr8(Qt + off, second), tr8(Gt + off, second), elem8{}, elem8{}};
     };
     Ops tc = tops(0);
 #pragma unroll
@@ -624,15 +626,15 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
   fetch(kt_lo, lds, lds + 2 * TILE);
 
   // Q~ and dO of this lane's query as B operands: chunk c holds dims 16c + 8hh .. +7.
-  bf16x8 qreg[D / 16], greg[D / 16];
+  elem8 qreg[D / 16], greg[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     const int d0 = 16 * c + 8 * hh;
     u32x4 wq = *reinterpret_cast<const u32x4*>(qb + (int64_t)qc * qstr + d0);
     u32x4 wg = *reinterpret_cast<const u32x4*>(gb + (int64_t)qc * p.sdo.s + d0);
     if (qi >= S) wq = wg = u32x4{0u, 0u, 0u, 0u};
-    qreg[c] = __builtin_bit_cast(bf16x8, wq);
-    greg[c] = __builtin_bit_cast(bf16x8, wg);
+    qreg[c] = __builtin_bit_cast(elem8, wq);
+    greg[c] = __builtin_bit_cast(elem8, wg);
   }
   const float nl = qi < S ? p.nlse[(int64_t)bh * S + qi] : 0.0f;
   const float dl = qi < S ? p.delta[(int64_t)bh * S + qi] : 0.0f;
@@ -675,16 +677,16 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     for (int blk = 0; blk < 2; ++blk) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
       // K~ / V rows of dims step c, read one step ahead of their MFMAs.
-      auto rows = [&](int c, bf16x8& kr, bf16x8& vr) {
+      auto rows = [&](int c, elem8& kr, elem8& vr) {
         const int off = 8 * (ql * C + ((2 * c + hh) ^ rsw)) + 32 * blk * D;
         kr = lds_read8(Kc + off);
         vr = lds_read8(Vc + off);
       };
-      bf16x8 kc_, vc_;
+      elem8 kc_, vc_;
       rows(0, kc_, vc_);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        bf16x8 kn = kc_, vn = vc_;
+        elem8 kn = kc_, vn = vc_;
         if (c + 1 < D / 16) rows(c + 1, kn, vn);
         sacc = mfma32x32x16(kc_, qreg[c], sacc);
         dpacc = mfma32x32x16(vc_, greg[c], dpacc);
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
       } else {
         pds(std::false_type{});
       }
-      bf16x8 sb[2];
+      elem8 sb[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         float sv[8];
@@ -725,10 +727,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
         const int kc = 2 * blk + g / NB, db = g % NB;
         return tr8(Kc + taddr[0][db] + 16 * kc * D, taddr[1][db] - taddr[0][db]);
       };
-      bf16x8 ka = kt_op(0);
+      elem8 ka = kt_op(0);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const bf16x8 kn = g + 1 < NG ? kt_op(g + 1) : ka;
+        const elem8 kn = g + 1 < NG ? kt_op(g + 1) : ka;
         dqacc[g % NB] = mfma32x32x16(ka, sb[g / NB], dqacc[g % NB]);
         ka = kn;
       }
@@ -895,8 +897,10 @@ hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
 }
 
 }  // namespace
+}  // namespace NEOX_ELEM_NS
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+hipError_t NEOX_ELEM_FN(launch_bwd)(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+  using namespace NEOX_ELEM_NS;
   switch (p.a.D) {
     case 64: return launch_d<64>(p, st, ev);
     case 96: return launch_d<96>(p, st, ev);
@@ -905,7 +909,9 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t*
   }
 }
 
+#if !NEOX_ELEM_F16  // one definition: the fp32 path's finalize (fp32 outputs)
 hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, float dq_scale) {
+  using namespace NEOX_ELEM_NS;
   const dim3 blk(256);
   switch (p.a.D) {
     case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), row_grid<64>(p), blk, 0, st, p, out_f32, dq_scale); break;
@@ -915,5 +921,6 @@ hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, f
   }
   return hipGetLastError();
 }
+#endif
 
 }  // namespace neox

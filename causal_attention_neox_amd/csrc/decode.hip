@@ -86,6 +86,28 @@ struct Elem<uint16_t> {  // bf16 storage
     *p = __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
   }
 };
+struct half_t {  // IEEE half storage
+  uint16_t bits;
+};
+template <>
+struct Elem<half_t> {
+  static constexpr int W = 4;
+  static __device__ __forceinline__ void load8(const half_t* p, uint32_t* w) {
+    const u32x4 x = ld16(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = x[e];
+  }
+  static __device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  }
+  static __device__ __forceinline__ float get(const uint32_t* w, int e) {
+    return h2f((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+  }
+  static __device__ __forceinline__ float load1(const half_t* p) { return h2f(p->bits); }
+  static __device__ __forceinline__ void store1(half_t* p, float x) {
+    p->bits = __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+  }
+};
 template <>
 struct Elem<float> {  // fp32 storage
   static constexpr int W = 8;
@@ -408,7 +430,12 @@ void decode_plan(int BH, int cap, int* chunk, int* nsplit) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {
-  return p.bf16 ? launch_decode_t<uint16_t>(p, st) : launch_decode_t<float>(p, st);
+  switch (p.dtype) {
+    case 0: return launch_decode_t<float>(p, st);
+    case 1: return launch_decode_t<uint16_t>(p, st);
+    case 2: return launch_decode_t<half_t>(p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace neox

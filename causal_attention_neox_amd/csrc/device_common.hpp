@@ -12,6 +12,8 @@ namespace neox {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -20,33 +22,69 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// bfloat16 bit patterns (low / high half of a dword) to float.
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32) in one dword.
+// The 16-bit storage element of the matrix kernels.  Their sources are compiled
+// once per type: bfloat16 by default, IEEE half when the translation unit
+// defines NEOX_ELEM_F16 to 1 before including this header.  elem8 is the MFMA
+// operand of 8 elements; el_lo / el_hi / el2f widen to float, pack2 / pack8
+// round to nearest even.
+#ifndef NEOX_ELEM_F16
+#define NEOX_ELEM_F16 0
+#endif
+#if NEOX_ELEM_F16
+typedef f16x8 elem8;
+typedef f16x2 elem2;
+typedef _Float16 elem1;
+__device__ __forceinline__ float el2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(elem8 a, elem8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+#else
+typedef bf16x8 elem8;
+typedef bf16x2 elem2;
+typedef __bf16 elem1;
+__device__ __forceinline__ float el2f(uint32_t bits16) { return bf2f(bits16); }
+__device__ __forceinline__ f32x16 mfma32x32x16(elem8 a, elem8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+#endif
+// Name of a launcher compiled for the element type (name_bf16 or name_f16), and
+// the namespace holding that type's kernels (their symbols differ per type).
+#if NEOX_ELEM_F16
+#define NEOX_ELEM_FN(name) name##_f16
+#define NEOX_ELEM_NS f16
+#else
+#define NEOX_ELEM_FN(name) name##_bf16
+#define NEOX_ELEM_NS bf16
+#endif
+__device__ __forceinline__ float el_lo(uint32_t w) { return el2f(w & 0xffffu); }
+__device__ __forceinline__ float el_hi(uint32_t w) { return el2f(w >> 16); }
+
+// Two floats -> two elements in one dword.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  bf16x2 v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
+  elem2 v;
+  v[0] = (elem1)a;
+  v[1] = (elem1)b;
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* x) {
+__device__ __forceinline__ elem8 pack8(const float* x) {
   u32x4 w;
   w[0] = pack2(x[0], x[1]);
   w[1] = pack2(x[2], x[3]);
   w[2] = pack2(x[4], x[5]);
   w[3] = pack2(x[6], x[7]);
-  return __builtin_bit_cast(bf16x8, w);
+  return __builtin_bit_cast(elem8, w);
 }
 
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 lds_read8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ elem8 lds_read8(const uint16_t* p) {
+  return __builtin_bit_cast(elem8, *reinterpret_cast<const u32x4*>(p));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -90,7 +128,7 @@ __device__ __forceinline__ void rotate8_scalar(const uint16_t* row, int d0, floa
   for (int e = 0; e < 8; ++e) {
     const int d = d0 + e;
     const bool in = d < rd, first = d < half;
-    xp[e] = bf2f(row[in ? (first ? d + half : d - half) : d]);
+    xp[e] = el2f(row[in ? (first ? d + half : d - half) : d]);
     cs[e] = rope[(int64_t)pos * half + (in ? (first ? d : d - half) : 0)];
   }
 #pragma unroll

@@ -1,4 +1,5 @@
-// Forward attention on gfx950, bf16 storage, bf16 MFMA with fp32 accumulation.
+// Forward attention on gfx950, 16-bit storage (bf16; fwd_f16.hip compiles this
+// file again for IEEE half), MFMA on that type with fp32 accumulation.
 //
 // Tiled, IO-aware exact attention (the FlashAttention-2 form the GPT-NeoX pages
 // name in "GPT-NeoX 开源训练框架深度解读", section "问题二：注意力计算太慢"):
@@ -36,6 +37,7 @@
 #include "device_common.hpp"
 
 namespace neox {
+namespace NEOX_ELEM_NS {
 namespace {
 
 constexpr int BM = 128;  // query rows per workgroup (4 waves x 32)
@@ -212,7 +214,7 @@ struct TilePlan {
           for (int e2 = 0; e2 < W / 2; ++e2) {
             const f32x4 c = cs[e2];  // (cos, sin) of pairs p0 + 2 e2 and p0 + 2 e2 + 1
             const uint32_t a = plo[i][e2], bw = phi[i][e2];
-            const float x1a = bf_lo(a), x1b = bf_hi(a), x2a = bf_lo(bw), x2b = bf_hi(bw);
+            const float x1a = el_lo(a), x1b = el_hi(a), x2a = el_lo(bw), x2b = el_hi(bw);
             lo[e2] = pack2(x1a * c[0] - x2a * c[1], x1b * c[2] - x2b * c[3]);
             hi[e2] = pack2(x2a * c[0] + x1a * c[1], x2b * c[2] + x1b * c[3]);
           }
@@ -238,8 +240,8 @@ struct TilePlan {
           float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] = bf_lo(w[e]);
-            x[2 * e + 1] = bf_hi(w[e]);
+            x[2 * e] = el_lo(w[e]);
+            x[2 * e + 1] = el_hi(w[e]);
           }
           rotate8_scalar(kb + (int64_t)r * ks, 8 * c, x, r, rd, rope);
           w = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
@@ -257,7 +259,7 @@ struct FwdState {
   static constexpr int TILE = BN * D;
   uint16_t* lds;
   TilePlan<D, ROT> tp;
-  bf16x8 qreg[D / 16];
+  elem8 qreg[D / 16];
   f32x16 oacc[D / 32];
   float m_ref, l_run;
   // LDS element offsets (from lds) of this lane's operand reads in the current
@@ -287,10 +289,10 @@ struct FwdState {
       const bool need_mask = !__all(lane_full);
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       // K~ operands are read one dims step ahead of the MFMAs using them.
-      bf16x8 k0c = lds_read8(lds + kaddr[0]), k1c = lds_read8(lds + kaddr[0] + 32 * D);
+      elem8 k0c = lds_read8(lds + kaddr[0]), k1c = lds_read8(lds + kaddr[0] + 32 * D);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        bf16x8 k0n = k0c, k1n = k1c;
+        elem8 k0n = k0c, k1n = k1c;
         if (c + 1 < D / 16) {
           k0n = lds_read8(lds + kaddr[c + 1]);
           k1n = lds_read8(lds + kaddr[c + 1] + 32 * D);
@@ -352,9 +354,9 @@ struct FwdState {
         const uint16_t* vp = lds + vaddr[g % NDB] + 16 * (g / NDB) * 8 * CPR;
         const s16x4 v0 = lds_read_tr4(vp);
         const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(elem8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8 pb[BN / 16];
+      elem8 pb[BN / 16];
 #pragma unroll
       for (int cp = 0; cp < BN / 16; ++cp) {
         float pv[8];
@@ -362,10 +364,10 @@ struct FwdState {
         for (int e = 0; e < 8; ++e) pv[e] = sacc[cp >> 1][8 * (cp & 1) + e];
         pb[cp] = pack8(pv);
       }
-      bf16x8 vcur = vread(0);
+      elem8 vcur = vread(0);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const bf16x8 vnext = g + 1 < NG ? vread(g + 1) : vcur;
+        const elem8 vnext = g + 1 < NG ? vread(g + 1) : vcur;
         oacc[g % NDB] = mfma32x32x16(vcur, pb[g / NDB], oacc[g % NDB]);
         vcur = vnext;
       }
@@ -459,8 +461,8 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf_lo(w[e]);
-        x[2 * e + 1] = bf_hi(w[e]);
+        x[2 * e] = el_lo(w[e]);
+        x[2 * e + 1] = el_hi(w[e]);
       }
       if (QROT) rotate8_scalar(qrow, d0, x, qc, a.rd, a.rope);
       if (qi >= S) {
@@ -592,8 +594,8 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf_lo(w[n][t][e]);
-          x[2 * e + 1] = bf_hi(w[n][t][e]);
+          x[2 * e] = el_lo(w[n][t][e]);
+          x[2 * e + 1] = el_hi(w[n][t][e]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
           if (d < rd) {
             const bool first = d < half;
             const float sn = first ? -cs[n][e].y : cs[n][e].y;  // rotate-half: (-x2, x1)
-            x[e] = fmaf(bf2f(rowbuf[wave][n][rw][t][first ? d + half : d - half]), sn,
+            x[e] = fmaf(el2f(rowbuf[wave][n][rw][t][first ? d + half : d - half]), sn,
                         x[e] * cs[n][e].x);
           }
         }
@@ -652,8 +654,10 @@ hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) 
 }
 
 }  // namespace
+}  // namespace NEOX_ELEM_NS
 
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+hipError_t NEOX_ELEM_FN(launch_fwd)(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) {
+  using namespace NEOX_ELEM_NS;
   switch (p.a.D) {
     case 64: return launch_dim<64>(p, st, ev);
     case 96: return launch_dim<96>(p, st, ev);

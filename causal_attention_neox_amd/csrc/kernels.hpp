@@ -35,8 +35,8 @@ struct FwdParams {
   float* lse;
   Strides sq, sk, sv, so;
   int out_f32;     // o stored as fp32
-  uint16_t* qrot;  // bf16 [B][H][S][D] workspace parts for q~ = R q and k~ = R k,
-  uint16_t* krot;  // or null (bf16 path; rotation then happens in the kernel)
+  uint16_t* qrot;  // 16-bit [B][H][S][D] workspace parts for q~ = R q and k~ = R k,
+  uint16_t* krot;  // or null (16-bit paths; rotation then happens in the kernel)
 };
 
 struct BwdParams {
@@ -53,8 +53,8 @@ struct BwdParams {
   float* dq_acc;   // [B][H][S][D] fp32 workspace (contiguous; fp32 path only)
   float* delta;    // [B][H][S] fp32 workspace: dO_i . o_i
   float* nlse;     // [B][H][S] fp32 workspace: -lse_i * log2(e) (ALiBi: also - slope * log2(e) * i)
-  uint16_t* qrot;  // [B][H][S][D] bf16 workspace: rotated q (bf16 path with rotary)
-  uint16_t* krot;  // [B][H][S][D] bf16 workspace: rotated k
+  uint16_t* qrot;  // [B][H][S][D] 16-bit workspace: rotated q (16-bit paths with rotary)
+  uint16_t* krot;  // [B][H][S][D] 16-bit workspace: rotated k
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int out_f32;     // dq, dk, dv stored as fp32
 };
@@ -65,7 +65,7 @@ struct DecodeParams {
   int rd;                 // rotary dims (0 = none)
   const float2* rope;     // [cap][rd/2] (cos, sin) or null when rd == 0
   float scale_log2;       // softmax scale * log2(e)
-  int bf16;               // 1: bf16 storage, 0: fp32
+  int dtype;              // storage: 0 fp32, 1 bf16, 2 fp16 (the NEOX_* codes)
   int chunk;              // cache rows per split workgroup (a multiple of decode_tile_rows())
   int nsplit;             // chunks per (batch, head) = ceil(cap / chunk)
   const int32_t* lens;    // [B] tokens already cached = position of the new token
@@ -90,11 +90,13 @@ hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStrea
 // the launcher records [1] after the q/k rotation pass (before the attention
 // kernel when there is none); the caller records [2] after the call.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev);
+hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
 
 // `ev` is null or 4 events recorded before the preprocess kernel, after it,
 // after the dK/dV kernel and at the end (after the dQ kernel or finalize).
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 
 // dq = dq_scale * R^T dQ~ from the fp32 accumulator, cast; shared by both paths

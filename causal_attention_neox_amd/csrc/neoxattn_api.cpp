@@ -103,7 +103,7 @@ int validate_common(const neox_attn_args* a) {
   if (!a) return NEOX_E_ARG;
   if (a->B < 1 || a->H < 1 || a->S < 1 || a->D < 1) return NEOX_E_ARG;
   if ((int64_t)a->B * a->H * a->S >= kMaxRows) return NEOX_E_ARG;
-  if (a->dtype != NEOX_F32 && a->dtype != NEOX_BF16) return NEOX_E_ARG;
+  if (a->dtype != NEOX_F32 && a->dtype != NEOX_BF16 && a->dtype != NEOX_F16) return NEOX_E_ARG;
   if (a->pos != NEOX_POS_NONE && a->pos != NEOX_POS_ROPE && a->pos != NEOX_POS_ALIBI)
     return NEOX_E_ARG;
   if (!finite_pos(a->softmax_scale)) return NEOX_E_ARG;
@@ -240,8 +240,9 @@ int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   if (st != NEOX_OK) return st;
   const neox_strides def = contiguous(a);
   const neox_strides* s = a->strides;
-  const int unit_in = a->dtype == NEOX_BF16 ? 8 : 4;
-  const int unit_out = (a->dtype == NEOX_BF16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
+  const bool half16 = a->dtype != NEOX_F32;  // bf16 or fp16 storage
+  const int unit_in = half16 ? 8 : 4;
+  const int unit_out = (half16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
   if ((st = check_tensor(q, s ? s[0] : def, unit_in)) != NEOX_OK) return st;
   if ((st = check_tensor(k, s ? s[1] : def, unit_in)) != NEOX_OK) return st;
   if ((st = check_tensor(v, s ? s[2] : def, unit_in)) != NEOX_OK) return st;
@@ -280,8 +281,8 @@ int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
   if (neox::record_event(ev, 0, hs) != hipSuccess) return NEOX_E_LAUNCH;
   hipError_t e;
-  if (a->dtype == NEOX_BF16) {
-    e = neox::launch_fwd_bf16(p, hs, ev);
+  if (a->dtype != NEOX_F32) {
+    e = a->dtype == NEOX_BF16 ? neox::launch_fwd_bf16(p, hs, ev) : neox::launch_fwd_f16(p, hs, ev);
   } else {
     e = neox::record_event(ev, 1, hs);
     if (e == hipSuccess) e = neox::launch_fwd_f32(p, hs);
@@ -297,8 +298,9 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   if (st != NEOX_OK) return st;
   const neox_strides def = contiguous(a);
   const neox_strides* s = a->strides;
-  const int unit_in = a->dtype == NEOX_BF16 ? 8 : 4;
-  const int unit_out = (a->dtype == NEOX_BF16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
+  const bool half16 = a->dtype != NEOX_F32;  // bf16 or fp16 storage
+  const int unit_in = half16 ? 8 : 4;
+  const int unit_out = (half16 && a->out_dtype == NEOX_OUT_SAME) ? 8 : 4;
   const void* ins[5] = {q, k, v, o, dout};
   for (int t = 0; t < 5; ++t)
     if ((st = check_tensor(ins[t], s ? s[t] : def, unit_in)) != NEOX_OK) return st;
@@ -349,8 +351,9 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   p.sdv = to_internal(s ? s[7] : def);
   p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
-  const hipError_t e = a->dtype == NEOX_BF16 ? neox::launch_bwd_bf16(p, hs, ev)
-                                             : neox::launch_bwd_f32(p, hs, ev);
+  const hipError_t e = a->dtype == NEOX_BF16  ? neox::launch_bwd_bf16(p, hs, ev)
+                       : a->dtype == NEOX_F16 ? neox::launch_bwd_f16(p, hs, ev)
+                                              : neox::launch_bwd_f32(p, hs, ev);
   return e == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
 }
 
@@ -403,7 +406,7 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
                           size_t workspace_bytes, void* stream) {
   if (B < 1 || H < 1 || D < 1 || cap < 1) return NEOX_E_ARG;
   if ((int64_t)B * H * cap >= kMaxRows) return NEOX_E_ARG;
-  if (dtype != NEOX_F32 && dtype != NEOX_BF16) return NEOX_E_ARG;
+  if (dtype != NEOX_F32 && dtype != NEOX_BF16 && dtype != NEOX_F16) return NEOX_E_ARG;
   if (rotary_dim < 0 || rotary_dim > D || (rotary_dim & 1)) return NEOX_E_ARG;
   if (rotary_dim > 0 && !finite_pos(rope_base)) return NEOX_E_ARG;
   if (!finite_pos(softmax_scale)) return NEOX_E_ARG;
@@ -434,7 +437,7 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   p.rd = rotary_dim;
   p.rope = rope;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  p.bf16 = dtype == NEOX_BF16 ? 1 : 0;
+  p.dtype = dtype;
   neox::decode_plan(B * H, cap, &p.chunk, &p.nsplit);
   p.lens = cache_lens;
   p.q = q;

@@ -16,8 +16,8 @@ Shapes follow the GPT-NeoX pages:
 
 Recipe (every workload): numpy ``SeedSequence(seed).spawn(5)`` gives independent
 streams for q, k, v, dO and the document lengths; q, k, v, dO are N(0, 1) draws
-in float64, multiplied by ``amp``, cast to float32 and, for bf16 workloads,
-rounded to bfloat16 with round-to-nearest-even.  Document lengths are drawn per
+in float64, multiplied by ``amp``, cast to float32 and, for bf16 (f16)
+workloads, rounded to bfloat16 (IEEE half) with round-to-nearest-even.  Document lengths are drawn per
 batch row from that row's own child stream.
 """
 
@@ -29,6 +29,7 @@ from typing import Optional
 import numpy as np
 
 BF16 = "bf16"
+F16 = "f16"
 F32 = "f32"
 
 
@@ -42,7 +43,7 @@ class Workload:
     S: int
     D: int
     rotary_dim: int
-    dtype: str  # "bf16" or "f32": storage type of q, k, v, o, dO
+    dtype: str  # "bf16", "f16" or "f32": storage type of q, k, v, o, dO
     backward: bool = True
     rope_base: float = 10000.0
     causal: bool = True
@@ -122,12 +123,21 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def storage_to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values (uint16 bits for bf16 / f16, float32 for f32) widened exactly."""
+    if dtype == BF16:
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    if dtype == F16:
+        return np.asarray(arr, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return np.asarray(arr).astype(np.float64)
+
+
 @dataclasses.dataclass
 class Inputs:
     """Generated tensors of one workload.
 
-    ``q, k, v, dout`` are the storage values: uint16 bf16 bit patterns for bf16
-    workloads, float32 for f32 workloads, shaped [B, H, S, D].  ``doc_offsets``
+    ``q, k, v, dout`` are the storage values: uint16 bit patterns for bf16 and
+    f16 workloads, float32 for f32 workloads, shaped [B, H, S, D].  ``doc_offsets``
     is int32 [B, n_docs_max + 1] (0 first, S last, non-decreasing; rows with
     fewer documents repeat S), or None for one document per row.
     """
@@ -144,9 +154,7 @@ class Inputs:
         a = getattr(self, name)
         if a is None:
             return None
-        if self.wl.dtype == BF16:
-            return bf16_bits_to_f32(a).astype(np.float64)
-        return a.astype(np.float64)
+        return storage_to_f64(a, self.wl.dtype)
 
 
 def pack_documents(rng: np.random.Generator, S: int, lo: int, hi: int) -> list:
@@ -182,6 +190,8 @@ def _draw(rng: np.random.Generator, shape, amp: float, dtype: str) -> np.ndarray
     x32 = x.astype(np.float32)
     if dtype == BF16:
         return round_to_bf16_bits(x32)
+    if dtype == F16:
+        return x32.astype(np.float16).view(np.uint16)  # round to nearest even
     return x32
 
 
@@ -288,10 +298,7 @@ class DecodeInputs:
     lens: np.ndarray
 
     def as_f64(self, name: str) -> np.ndarray:
-        a = getattr(self, name)
-        if self.wl.dtype == BF16:
-            return bf16_bits_to_f32(a).astype(np.float64)
-        return a.astype(np.float64)
+        return storage_to_f64(getattr(self, name), self.wl.dtype)
 
 
 def generate_decode(wl: DecodeWorkload) -> DecodeInputs:
@@ -318,6 +325,6 @@ def decode_bytes(wl: DecodeWorkload, lens) -> int:
     cached key and value rows it attends over (the new row included) once;
     the new token's q, k, v are read, its key and value written into the
     cache, and o and the fp32 lse written."""
-    es = 2 if wl.dtype == BF16 else 4
+    es = 4 if wl.dtype == F32 else 2
     rows = sum(int(t) + 1 for t in lens) * wl.H
     return rows * 2 * wl.D * es + wl.B * wl.H * (6 * wl.D * es + 4)

@@ -41,7 +41,7 @@
  *  - Supported: D in {64, 96, 128}; 0 <= rotary_dim <= D, rotary_dim even;
  *    rope_base > 0 and finite; softmax_scale > 0 and finite; B, H, S >= 1;
  *    B*H*S < 2^31; tensor base pointers 16-byte aligned; row strides multiples
- *    of 8 elements (bf16) or 4 elements (fp32).
+ *    of 8 elements (bf16, fp16) or 4 elements (fp32).
  *  - Rotary cos/sin table: the first call on a device for a (rotary_dim,
  *    rope_base) pair, or for a longer S than that pair has seen, allocates a
  *    table of S * rotary_dim * 4 bytes on the device and fills it (angles and
@@ -72,6 +72,7 @@ extern "C" {
 /* Storage type of q, k, v, o, dout (and of dq, dk, dv unless out_dtype says fp32). */
 #define NEOX_F32 0
 #define NEOX_BF16 1
+#define NEOX_F16 2 /* IEEE half ("FasterTransformer GPT-NeoX 推理指南": FP16 inference) */
 
 /* Position scheme. */
 #define NEOX_POS_NONE 0
@@ -134,7 +135,7 @@ typedef struct neox_attn_args {
 const char* neox_status_str(int status);
 
 /*
- * Bytes of the optional forward workspace: two bf16 [B, H, S, D] buffers that
+ * Bytes of the optional forward workspace: two 16-bit [B, H, S, D] buffers that
  * receive the rotated rows q~ = R q and k~ = R k (NeoX rotate-half with each
  * row's own position; "FasterTransformer GPT-NeoX 推理指南", section
  * "模型配置": both Q and K are rotated), written by one row pass so that the
@@ -152,9 +153,10 @@ size_t neox_rope_attn_fwd_workspace_size(int B, int H, int S, int D);
  * backward needs it).  rotary_dim = 0 turns the rotation off.  Causal masking
  * when causal != 0.  workspace: NULL, or caller-owned device memory of at
  * least neox_rope_attn_fwd_workspace_size() bytes, 256-byte aligned,
- * overwritten by the call; it is used by the bf16 path with rotary_dim > 0
- * (the faster path) and ignored otherwise.  Results do not depend on whether
- * a workspace is given beyond fp32 rounding order of the rotation.
+ * overwritten by the call; it is used by the bf16 and fp16 paths with
+ * rotary_dim > 0 (the faster path) and ignored otherwise.  Results do not
+ * depend on whether a workspace is given beyond fp32 rounding order of the
+ * rotation.
  */
 int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int S, int D, int rotary_dim, float rope_base,
@@ -164,9 +166,9 @@ int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, flo
 /* Bytes of device workspace the backward needs, in five 256-byte aligned
  * parts: an fp32 [B, H, S, D] dq accumulator, two fp32 [B, H, S] row terms
  * (the softmax-gradient row sum and the negated base-2 log-sum-exp), and the
- * rotated q and k as bf16, [B, H, S, D] each (used by the bf16 path only; the
- * size does not depend on dtype) -- B*H*S*(8D + 8) bytes up to rounding,
- * linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
+ * rotated q and k in the 16-bit storage type, [B, H, S, D] each (used by the
+ * bf16 and fp16 paths only; the size does not depend on dtype) -- B*H*S*(8D + 8)
+ * bytes up to rounding, linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
 size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
 
 /*
@@ -175,8 +177,8 @@ size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
  * `dtype`) are written and must not alias the inputs.  workspace: device
  * memory of at least neox_rope_attn_bwd_workspace_size() bytes, 256-byte
  * aligned, owned by the caller, overwritten by the call (its contents
- * afterwards are unspecified).  The bf16 path is deterministic (dq, dk and dv
- * are each reduced by one workgroup, in a fixed order); the fp32 path
+ * afterwards are unspecified).  The bf16 and fp16 paths are deterministic (dq,
+ * dk and dv are each reduced by one workgroup, in a fixed order); the fp32 path
  * accumulates dq with fp32 atomics, so its last bits may vary run to run.
  */
 int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -33,9 +33,14 @@ def torch():
 
 
 def _dev(torch, arr, dtype):
-    if dtype == W.BF16:
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype in (W.BF16, W.F16):
+        tdt = torch.bfloat16 if dtype == W.BF16 else torch.float16
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(tdt).cuda()
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def _np_bits(arr, dtype):
+    return arr.view(np.int32) if dtype == W.F32 else arr.view(np.int16)
 
 
 def _f64(t):
@@ -45,7 +50,7 @@ def _f64(t):
 def _bits(t):
     """Storage bits of a device tensor as a numpy array (exact comparisons)."""
     import torch
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.detach().cpu().view(torch.int16).numpy()
     return t.detach().cpu().numpy().view(np.int32)
 
@@ -63,7 +68,7 @@ def _check(name, got, ref, dtype, label):
 
 def _run(torch, neox, wl, q, k, v, kc, vc, lens, stream=None):
     B, H, D, cap = wl.B, wl.H, wl.D, wl.cap
-    odt = torch.bfloat16 if wl.dtype == W.BF16 else torch.float32
+    odt = {W.BF16: torch.bfloat16, W.F16: torch.float16}.get(wl.dtype, torch.float32)
     o = torch.empty((B, H, D), dtype=odt, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(neox.neox_rope_attn_decode_workspace_size(B, H, D, cap), dtype=torch.uint8,
@@ -84,6 +89,8 @@ STEP_CASES = [
     (64, 64, "f32"),
     (96, 24, "f32"),
     (128, 128, "f32"),
+    (96, 24, "f16"),
+    (128, 40, "f16"),
 ]
 
 
@@ -143,15 +150,20 @@ def test_decode_steps_every_element(torch, case):
         assert np.array_equal(vc_bits[b][:, rows], v_bits[b]), "value rows must be copied exactly"
         # rows outside the written range are untouched
         keep = np.setdiff1d(np.arange(cap), rows)
-        kb0 = cache.k_cache.view(np.int16) if dtype == W.BF16 else cache.k_cache.view(np.int32)
-        assert np.array_equal(_bits(kc)[b][:, keep], kb0[b][:, keep])
+        assert np.array_equal(_bits(kc)[b][:, keep], _np_bits(cache.k_cache, dtype)[b][:, keep])
+
+
+FULL_CASES = [(n, None) for n in sorted(W.DECODE_WORKLOADS)] + [
+    ("neox20b_decode_b8_cap2048_ragged", W.F16)]
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", sorted(W.DECODE_WORKLOADS))
-def test_decode_full_size_every_head(torch, name):
+@pytest.mark.parametrize("name,dtype", FULL_CASES, ids=[f"{n}-{d or 'bf16'}" for n, d in FULL_CASES])
+def test_decode_full_size_every_head(torch, name, dtype):
     import causal_attention_neox_amd as neox
     wl = W.DECODE_WORKLOADS[name]
+    if dtype is not None:
+        wl = wl.with_sizes(dtype=dtype)
     inp = W.generate_decode(wl)
     print(f"[decode] full {name} lens={inp.lens.tolist()}", flush=True)
     dt = wl.dtype
@@ -177,9 +189,7 @@ def test_decode_full_size_every_head(torch, name):
 
     kc_got = _f64(kc)
     kb, vb = _bits(kc), _bits(vc)
-    kb0 = inp.k_cache.view(np.int16) if dt == W.BF16 else inp.k_cache.view(np.int32)
-    vb0 = inp.v_cache.view(np.int16) if dt == W.BF16 else inp.v_cache.view(np.int32)
-    vnew = inp.v.view(np.int16) if dt == W.BF16 else inp.v.view(np.int32)
+    kb0, vb0, vnew = (_np_bits(a, dt) for a in (inp.k_cache, inp.v_cache, inp.v))
     for b in range(wl.B):
         t = int(inp.lens[b])
         _check("k_cache row", kc_got[b, :, t], ref_k[b], dt, f"{name} b{b}")

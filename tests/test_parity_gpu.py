@@ -51,6 +51,15 @@ SMALL = [
     (2, 2, 130, 96, 24, "f32", True, False),
     (1, 2, 200, 128, 128, "f32", True, False),
     (1, 2, 100, 128, 10, "f32", False, True),
+    # fp16 storage: the same kernels compiled for IEEE half
+    (1, 2, 3, 96, 24, "f16", True, False),
+    (1, 3, 33, 64, 2, "f16", True, False),
+    (2, 2, 65, 128, 0, "f16", True, False),
+    (1, 2, 129, 96, 96, "f16", True, False),
+    (2, 2, 300, 128, 128, "f16", True, False),
+    (1, 2, 257, 128, 40, "f16", True, False),
+    (1, 2, 190, 128, 128, "f16", False, False),
+    (1, 4, 300, 128, 0, "f16", True, True),
 ]
 
 
@@ -69,7 +78,7 @@ def test_small_shapes_every_element(case):
     ref = pu.oracle_heads(inp, heads)
     # With rotary in bf16 the forward has two key paths: keys pre-rotated by a
     # row pass into the workspace, or rotated at each tile visit (no workspace).
-    for fws in ((True, False) if dt == "bf16" and rd > 0 else (True,)):
+    for fws in ((True, False) if dt != "f32" and rd > 0 else (True,)):
         gpu = pu.run_library(inp, backward=True, fwd_workspace=fws)
         pu.compare(gpu, ref, heads, dt, label=f"{_id(case)} fwd_workspace={fws}")
 
@@ -102,6 +111,29 @@ def test_packed_documents_every_element(case):
         inp.wl = dataclasses.replace(wl, rope_doc_positions=True)
         ref = pu.oracle_heads(inp, heads)
         pu.compare(gpu, ref, heads, "bf16", label=f"docs S={S} D={D} document positions")
+
+
+def test_fp16_packed_documents_every_element():
+    S, D, rows = 200, 96, [[70, 1, 129], [64, 64, 64, 8]]
+    wl = pu.small_workload(2, 2, S, D, 24, dtype="f16", seed=S + D + 1)
+    inp = generate(wl, with_dout=True)
+    inp.doc_offsets = doc_offsets_from_lengths(rows, S)
+    heads = [(b, h) for b in range(2) for h in range(2)]
+    gpu = pu.run_library(inp, backward=True)
+    pu.compare(gpu, pu.oracle_heads(inp, heads), heads, "f16", label="f16 docs")
+
+
+@pytest.mark.timeout(900)
+def test_fp16_20b_layout_full_size_sampled_heads():
+    """The 20B head layout at full size (B=4, H=64, S=2048, D=96, rd=24) with
+    fp16 storage, as FasterTransformer runs GPT-NeoX, on sampled heads."""
+    wl = dataclasses.replace(WORKLOADS["neox20b_s2048_h64_d96_rd24"], dtype="f16")
+    inp = generate(wl)
+    gpu = pu.run_library(inp, backward=True)
+    for key, t in gpu.items():
+        assert bool(t.isfinite().all()), f"f16: non-finite {key}"
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    pu.compare(gpu, pu.oracle_heads(inp, heads), heads, "f16", label="f16 neox20b")
 
 
 def test_fp32_workload_full():
