@@ -41,7 +41,10 @@ notes of this repository):
   R7  lse is the natural-log logsumexp of the allowed scores of a row;
   R8  with packed documents the rotary positions are 0..S-1 along the batch row,
       or, when asked for (``rope_doc_positions``), the token's offset inside its
-      document, so that each packed document is rotated as if it stood alone.
+      document, so that each packed document is rotated as if it stood alone;
+  R22 the FP8 forward takes q, k, v as E4M3 codes with one scale per tensor, q
+      and k already rotated; its exact result is attention over the decoded
+      values times their scales.
 
 Pins (tests that fix this oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``: torch's float64 scaled_dot_product_attention and
@@ -334,3 +337,42 @@ def attn_decode(q, k, v, k_cache, v_cache, *, rotary_dim: int, rope_base: float 
     e = np.exp(s - m)
     l = e.sum()
     return (e / l) @ vals, m + np.log(l), k_rot
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) forward
+# --------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of FP8 E4M3 codes (the OCP 8-bit format with 1 sign bit, 4
+    exponent bits of bias 7 and 3 mantissa bits; no infinities, the codes with
+    all exponent and mantissa bits set are NaN): exponent field e > 0 gives
+    (-1)^s 2^(e-7) (1 + m/8), e = 0 gives the subnormal (-1)^s 2^-6 (m/8).
+    The pages name FP8 compute (Transformer Engine, "GPT-NeoX 开源训练框架深度解读",
+    the TE Dockerfile) without fixing a format; E4M3 is the reading (R22)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = np.ldexp(m / 8.0, -6)
+    v = s * np.where(e > 0, normal, sub)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, *,
+                 causal: bool = True, softmax_scale: Optional[float] = None,
+                 heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Forward of the FP8 variant: q, k, v given as E4M3 codes [B, H, S, D] with
+    one scale per tensor (value = decoded code x scale); q and k are already
+    rotated (the rotation is applied before quantisation, R22).  The exact
+    result is attention over the dequantised tensors, which is what this
+    returns (o, lse); the tolerance of an FP8 kernel against it comes from the
+    rounding of the probabilities to E4M3 (R23)."""
+    q = e4m3_decode(q8) * float(q_scale)
+    k = e4m3_decode(k8) * float(k_scale)
+    v = e4m3_decode(v8) * float(v_scale)
+    D = q.shape[-1]
+    return attn_fwd(q, k, v, rotary_dim=0, causal=causal,
+                    softmax_scale=1.0 / np.sqrt(D) if softmax_scale is None else softmax_scale,
+                    heads=heads)

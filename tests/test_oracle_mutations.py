@@ -13,7 +13,8 @@ from tests import test_oracle_pins as pins
 
 ORIG = {n: getattr(orc, n) for n in
         ("rope_rotate", "rope_inv_freq", "allowed_mask", "alibi_bias", "_head_probs",
-         "head_backward", "head_forward", "alibi_slopes", "attn_decode", "rope_positions")}
+         "head_backward", "head_forward", "alibi_slopes", "attn_decode", "rope_positions",
+         "e4m3_decode")}
 
 
 def _rotate_sign_flipped(x, positions, rotary_dim, base, inverse=False):
@@ -129,6 +130,16 @@ def _positions_off_by_one_at_documents(S, offsets_row=None, per_document=False):
     return np.where(pos > 0, pos - 1, pos) if per_document else pos  # slip: start at -1 / 0 twice
 
 
+def _e4m3_bias_eight(codes):
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    return ORIG["e4m3_decode"](c) / 2.0 * np.where((c >> 3) & 0xF, 1.0, 2.0)  # slip: bias 8
+
+
+def _e4m3_no_subnormals(codes):
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    return np.where((c >> 3) & 0xF, ORIG["e4m3_decode"](c), 0.0)  # slip: subnormals flushed
+
+
 MUTATIONS = {
     "rotation_sign": ("rope_rotate", _rotate_sign_flipped),
     "rotation_interleaved": ("rope_rotate", _rotate_interleaved),
@@ -147,6 +158,8 @@ MUTATIONS = {
     "k_unrotated": ("head_forward", _forward_k_unrotated),
     "decode_position_off_by_one": ("attn_decode", _decode_position_off_by_one),
     "document_positions_slip": ("rope_positions", _positions_off_by_one_at_documents),
+    "e4m3_exponent_bias": ("e4m3_decode", _e4m3_bias_eight),
+    "e4m3_flushes_subnormals": ("e4m3_decode", _e4m3_no_subnormals),
 }
 
 

@@ -476,3 +476,52 @@ def test_decode_appended_key_is_rotated_at_its_position():
     np.testing.assert_allclose(k_rot[:h], z.real, rtol=0, atol=1e-12)
     np.testing.assert_allclose(k_rot[h:rd], z.imag, rtol=0, atol=1e-12)
     np.testing.assert_array_equal(k_rot[rd:], k[rd:])
+
+
+# ---------------------------------------------------------------- FP8 (E4M3)
+
+def test_e4m3_decode_format_constants():
+    """Values fixed by the E4M3 definition: 1.0, the largest finite value
+    448 = 1.75 x 2^8, the smallest normal 2^-6, the smallest subnormal 2^-9,
+    signed zero, NaN codes, and 0.5 / 3.0 / -2.25."""
+    d = orc.e4m3_decode
+    assert d(0x38) == 1.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9
+    assert d(0x00) == 0.0 and d(0x80) == 0.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x30) == 0.5 and d(0x44) == 3.0 and d(0xC1) == -2.25
+
+
+def test_e4m3_decode_is_monotonic_with_three_mantissa_bits():
+    """Positive finite codes 0..126 decode to strictly increasing values; inside
+    each binade there are 8 evenly spaced values (3 mantissa bits)."""
+    v = orc.e4m3_decode(np.arange(127))
+    assert np.all(np.diff(v) > 0)
+    for e in range(1, 16):
+        block = v[8 * e: 8 * e + 8] if 8 * e + 8 <= 127 else v[8 * e: 127]
+        steps = np.diff(block)
+        np.testing.assert_allclose(steps, 2.0 ** (e - 7) / 8)
+
+
+def test_fp8_forward_is_attention_of_dequantised_inputs():
+    """The FP8 forward equals the exact forward over code x scale, with the
+    scales entering linearly: doubling v's scale doubles o, and halving q's
+    scale while doubling k's leaves everything unchanged."""
+    rng = np.random.default_rng(31)
+    B, H, S, D = 1, 2, 40, 16
+    q8, k8, v8 = (rng.integers(0, 256, (B, H, S, D)) for _ in range(3))
+    for c in (q8, k8, v8):
+        c[(c & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        c[(c & 0x78) > 0x58] &= 0xBF   # keep magnitudes moderate (exponent <= 11)
+    o, lse = orc.attn_fwd_fp8(q8, k8, v8, 0.05, 0.1, 0.5)
+    qd, kd, vd = (orc.e4m3_decode(c) * s for c, s in ((q8, 0.05), (k8, 0.1), (v8, 0.5)))
+    o2, lse2 = orc.attn_fwd(qd, kd, vd, rotary_dim=0)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, atol=1e-13)
+    o3, lse3 = orc.attn_fwd_fp8(q8, k8, v8, 0.05, 0.1, 1.0)
+    np.testing.assert_allclose(o3, 2.0 * o, atol=1e-12)
+    o4, lse4 = orc.attn_fwd_fp8(q8, k8, v8, 0.025, 0.2, 0.5)
+    np.testing.assert_allclose(o4, o, atol=1e-12)
+    np.testing.assert_allclose(lse4, lse, atol=1e-12)
