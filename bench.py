@@ -14,7 +14,8 @@ value = algorithmic fwd+bwd FLOP per step / time per step, in TFLOP/s:
 
 The JSON line also carries the roofline of the dominant kernel (timed live via
 per-phase HIP events recorded by the library on the launch stream), the forward
-efficiency at S=2048, D=128, the same step with fp16 storage, the decoding step's HBM rate (one new token per
+efficiency at S=2048, D=128, the same step with fp16 storage, the FP8 forward at
+S=2048, D=128, the decoding step's HBM rate (one new token per
 sequence against a 2048-row cache), and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 """
@@ -35,6 +36,8 @@ METRIC = "causal RoPE-attention fwd+bwd TFLOP/s at S=2048 (1 GPU) + % of bf16 MF
 # Dense bf16 (and fp16) MFMA peak of MI355X: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
+# Dense FP8 MFMA peak: twice the bf16 rate.
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 
 
 def parse():
@@ -49,6 +52,7 @@ def parse():
     ap.add_argument("--no-fwd-target", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with kernels of known traffic (scale for traffic counters)")
     return ap.parse_args()
@@ -188,6 +192,35 @@ def fp16_step(args, torch, np, neox, W, wl):
     return {"workload": wl.name, "dtype": "f16", "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
             "frac_of_f16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kms.items()}}
+
+
+def fp8_forward(args, torch, np, neox, W):
+    """The FP8 (E4M3) forward at S=2048, D=128 (B=4, H=32, causal), timed back
+    to back; algorithmic 4 D flop per allowed pair as for the 16-bit forward."""
+    wl = W.FP8_WORKLOADS[W.FP8_BENCH_WORKLOAD]
+    inp = W.generate_fp8(wl)
+    q8, k8, v8 = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (inp.q8, inp.k8, inp.v8))
+    o = torch.empty((wl.B, wl.H, wl.S, wl.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.B, wl.H, wl.S), dtype=torch.float32, device="cuda")
+    call = lambda: neox.neox_attn_fwd_fp8(q8, k8, v8, *inp.scales, o, lse,  # noqa: E731
+                                          causal=wl.causal, softmax_scale=wl.softmax_scale)
+    for _ in range(max(args.warmup, 2)):
+        call()
+    n = max(args.steps, 20)
+    start, end = make_events(torch, 2)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(n):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    flops = 4 * wl.D * wl.B * wl.H * W.allowed_pairs(wl.S, wl.causal)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "D": wl.D,
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 1),
+            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def decode(args, torch, np, neox, W):
@@ -362,6 +395,8 @@ def main():
         out["fwd_target"] = fwd_target(args, torch, np, neox, W)
     if not args.no_fp16:
         out["fp16"] = fp16_step(args, torch, np, neox, W, wl)
+    if not args.no_fp8:
+        out["fp8_fwd"] = fp8_forward(args, torch, np, neox, W)
     if not args.no_decode:
         out["decode"] = decode(args, torch, np, neox, W)
     if not args.no_cpu_baseline:

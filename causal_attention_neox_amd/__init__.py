@@ -25,7 +25,7 @@ __all__ = [
     "NeoxError", "neox_status_str", "neox_rope_attn_fwd", "neox_rope_attn_bwd",
     "neox_rope_attn_fwd_workspace_size", "neox_rope_attn_bwd_workspace_size",
     "neox_attn_fwd_ex", "neox_attn_bwd_ex",
-    "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode",
+    "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode", "neox_attn_fwd_fp8",
     "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
     "NEOX_F32", "NEOX_BF16", "NEOX_F16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
@@ -223,6 +223,24 @@ def neox_rope_attn_decode(q, k, v, k_cache, v_cache, cache_lens, o, lse, rotary_
         _ptr(lse), B, H, D, cap, int(rotary_dim), float(rope_base), scale, _dtype_code(q),
         _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "neox_rope_attn_decode")
+
+
+def neox_attn_fwd_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, o, lse,
+                      causal: bool = True, softmax_scale: Optional[float] = None,
+                      stream=None) -> None:
+    """Calls neox_attn_fwd_fp8: q8, k8, v8 are [B, H, S, D] tensors of E4M3 codes
+    (uint8 or torch.float8_e4m3fn), q8 and k8 already rotated; o is bf16 or fp32
+    [B, H, S, D]; lse is fp32 [B, H, S]."""
+    import torch
+    B, H, S, D = _shape(q8)
+    if o.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("o must be bfloat16 or float32")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().neox_attn_fwd_fp8(
+        _ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale), _ptr(o),
+        _ptr(lse), B, H, S, D, int(bool(causal)), scale,
+        NEOX_OUT_F32 if o.dtype == torch.float32 else NEOX_OUT_SAME, _stream(stream))
+    _check(st, "neox_attn_fwd_fp8")
 
 
 def neox_check_doc_offsets(offsets_host, S: int) -> int:

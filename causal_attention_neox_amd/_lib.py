@@ -70,6 +70,9 @@ SIGNATURES = {
                                       c_void_p, c_void_p, c_void_p,
                                       c_int, c_int, c_int, c_int, c_int, c_float, c_float,
                                       c_int, c_void_p, c_size_t, c_void_p]),
+    "neox_attn_fwd_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_float, c_float, c_float,
+                                  c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                  c_float, c_int, c_void_p]),
     "neox_check_doc_offsets": (c_int, [c_void_p, c_int, c_int, c_int]),
     "neox_rope_table_prepare": (c_int, [c_int, c_int, c_float]),
 }

@@ -80,6 +80,23 @@ struct DecodeParams {
                           // (unused when nsplit == 1)
 };
 
+// FP8 (E4M3) forward: q~, k~ (already rotated) and v as E4M3 codes [B][H][S][D],
+// contiguous; value = code x per-tensor scale.
+struct Fp8FwdParams {
+  int B, H, S, D;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;           // [B][H][S][D] bf16, or fp32 when out_f32
+  float* lse;        // [B][H][S]
+  float scale_log2;  // softmax scale * q scale * k scale * log2(e)
+  float v_scale;
+  int causal;
+  int out_f32;
+};
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t st);
+
 int decode_tile_rows();
 void decode_plan(int BH, int cap, int* chunk, int* nsplit);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);

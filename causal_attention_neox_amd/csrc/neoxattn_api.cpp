@@ -451,6 +451,43 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   return neox::launch_decode(p, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
 }
 
+int neox_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale,
+                      float k_scale, float v_scale, void* o, float* lse, int B, int H, int S,
+                      int D, int causal, float softmax_scale, int out_dtype, void* stream) {
+  if (B < 1 || H < 1 || S < 1 || D < 1) return NEOX_E_ARG;
+  if ((int64_t)B * H * S >= kMaxRows) return NEOX_E_ARG;
+  if (!finite_pos(q_scale) || !finite_pos(k_scale) || !finite_pos(v_scale)) return NEOX_E_ARG;
+  if (!finite_pos(softmax_scale)) return NEOX_E_ARG;
+  if (out_dtype != NEOX_OUT_SAME && out_dtype != NEOX_OUT_F32) return NEOX_E_ARG;
+  const void* ptrs[] = {q8, k8, v8, o, lse};
+  for (const void* ptr : ptrs) {
+    if (!ptr) return NEOX_E_ARG;
+    if (!aligned16(ptr)) return NEOX_E_ALIGN;
+  }
+  if (o == q8 || o == k8 || o == v8) return NEOX_E_ARG;
+  if (D != 64 && D != 96 && D != 128) return NEOX_E_UNSUPPORTED;
+  int dev = 0;
+  const int st = check_device(&dev);
+  if (st != NEOX_OK) return st;
+  neox::Fp8FwdParams p;
+  p.B = B;
+  p.H = H;
+  p.S = S;
+  p.D = D;
+  p.q = q8;
+  p.k = k8;
+  p.v = v8;
+  p.o = o;
+  p.lse = lse;
+  p.scale_log2 = softmax_scale * q_scale * k_scale * 1.4426950408889634f;
+  p.v_scale = v_scale;
+  p.causal = causal ? 1 : 0;
+  p.out_f32 = out_dtype == NEOX_OUT_F32 ? 1 : 0;
+  return neox::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? NEOX_OK
+             : NEOX_E_LAUNCH;
+}
+
 int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S) {
   if (!host_offsets || B < 1 || n_docs < 1 || S < 1) return NEOX_E_ARG;
   for (int b = 0; b < B; ++b) {

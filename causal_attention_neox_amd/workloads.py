@@ -328,3 +328,74 @@ def decode_bytes(wl: DecodeWorkload, lens) -> int:
     es = 4 if wl.dtype == F32 else 2
     rows = sum(int(t) + 1 for t in lens) * wl.H
     return rows * 2 * wl.D * es + wl.B * wl.H * (6 * wl.D * es + 4)
+
+
+# ---------------------------------------------------------------- FP8 (E4M3)
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the non-negative finite E4M3 codes 0..126: code = (e << 3) | m
+    is 2^(e-7) (1 + m/8) for e > 0 and 2^-6 m/8 for e = 0 (OCP FP8 E4M3)."""
+    code = np.arange(127)
+    e, m = code >> 3, code & 7
+    return np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 codes (uint8), round to nearest, ties to the even code,
+    saturating at +-448 (no NaN produced for finite inputs)."""
+    x = np.asarray(x, dtype=np.float64)
+    table = _e4m3_table()
+    a = np.minimum(np.abs(x), table[-1])
+    hi = np.clip(np.searchsorted(table, a, side="left"), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - table[lo], table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a <= 0, 0, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(x < 0, code | 0x80, code).astype(np.uint8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """FP8 forward problem: q~, k~ (already rotated) and v drawn N(0, 1), each
+    quantised to E4M3 with one scale per tensor, scale = amax / 448 (the
+    largest value maps to the largest code)."""
+
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal: bool = True
+    seed: int = 20260200
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    wl: Fp8Workload
+    q8: np.ndarray  # uint8 E4M3 codes [B, H, S, D]
+    k8: np.ndarray
+    v8: np.ndarray
+    scales: tuple   # (q, k, v)
+
+
+FP8_WORKLOADS = {
+    "fp8_s2048_d128": Fp8Workload("fp8_s2048_d128", B=4, H=32, S=2048, D=128, seed=20260201),
+    "fp8_neox20b_s2048_d96": Fp8Workload("fp8_neox20b_s2048_d96", B=4, H=64, S=2048, D=96,
+                                         seed=20260202),
+}
+FP8_BENCH_WORKLOAD = "fp8_s2048_d128"
+
+
+def generate_fp8(wl: Fp8Workload) -> Fp8Inputs:
+    """Seeded FP8 inputs: ``SeedSequence(seed).spawn(3)`` streams for q, k, v."""
+    out, scales = [], []
+    for s in np.random.SeedSequence(wl.seed).spawn(3):
+        x = np.random.default_rng(s).standard_normal((wl.B, wl.H, wl.S, wl.D))
+        scale = float(np.abs(x).max()) / 448.0
+        out.append(e4m3_encode(x / scale))
+        scales.append(scale)
+    return Fp8Inputs(wl, out[0], out[1], out[2], tuple(scales))

@@ -244,6 +244,27 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
                           size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 forward: causal (or full) attention with q~, k~ and v stored as FP8 E4M3
+ * codes (OCP format: bias 7, 3 mantissa bits, largest finite 448), one scale
+ * per tensor: value = code x scale.  The GPT-NeoX stack computes in FP8
+ * through Transformer Engine ("GPT-NeoX 开源训练框架深度解读", the TE image); in
+ * that arrangement the rotation comes before quantisation, so q8 and k8 hold
+ * the ROTATED projections (q~ = R q, k~ = R k, quantised by the caller).
+ *  q8, k8, v8  device [B, H, S, D] E4M3 codes, contiguous (read only).
+ *  o           device [B, H, S, D] bf16, or fp32 with out_dtype NEOX_OUT_F32.
+ *  lse         device [B, H, S] fp32, natural log (written).
+ * Both products run on the FP8 matrix cores with fp32 accumulation; the
+ * probabilities are rounded to E4M3 (scaled by 2^4) for the P V product, so o
+ * differs from exact attention over the dequantised inputs by at most about
+ * 2^-4 of sum_j p_j |v_j| per element (plus the output rounding).
+ * Supported: D in {64, 96, 128}; scales finite and > 0; pointers 16-byte
+ * aligned; B*H*S < 2^31.  Same status codes as the other entry points.
+ */
+int neox_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale,
+                      float k_scale, float v_scale, void* o, float* lse, int B, int H, int S,
+                      int D, int causal, float softmax_scale, int out_dtype, void* stream);
+
+/*
  * Host-side check of a HOST copy of doc_offsets ([B][n_docs + 1] int32):
  * returns NEOX_OK when every row starts at 0, never decreases and ends at S,
  * NEOX_E_ARG otherwise (or for a NULL pointer / bad sizes).  No device work.

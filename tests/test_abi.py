@@ -261,3 +261,24 @@ def test_decode_workspace_size(lib):
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present on this host")
 def test_valid_decode_without_gpu_fails_loudly(lib):
     assert dec(lib) == E_DEV
+
+
+def fp8(lib, q=A1, k=A2, v=A3, qs=0.01, ks=0.01, vs=0.01, o=A4, lse=A5, B=2, H=4, S=128, D=128,
+        causal=1, scale=0.088, out=0):
+    return lib.neox_attn_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, S, D, causal, scale, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_ARG), (dict(lse=None), E_ARG), (dict(B=0), E_ARG), (dict(S=0), E_ARG),
+    (dict(D=80), E_UNSUP), (dict(qs=0.0), E_ARG), (dict(vs=float("nan")), E_ARG),
+    (dict(ks=-1.0), E_ARG), (dict(scale=0.0), E_ARG), (dict(out=5), E_ARG),
+    (dict(o=A1), E_ARG), (dict(v=P(0x30008)), E_ALIGN), (dict(lse=P(0x50004)), E_ALIGN),
+    (dict(B=1 << 16, H=1 << 8, S=1 << 8), E_ARG),
+])
+def test_fp8_forward_validation(lib, kw, status):
+    assert fp8(lib, **kw) == status
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present on this host")
+def test_valid_fp8_forward_without_gpu_fails_loudly(lib):
+    assert fp8(lib) == E_DEV

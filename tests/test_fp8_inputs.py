@@ -1,0 +1,39 @@
+"""The E4M3 encoder of the input generator, checked against the format's
+definition (the oracle's decoder is a separate implementation)."""
+
+import numpy as np
+
+from causal_attention_neox_amd import workloads as W
+from oracle import neox_oracle as orc
+
+
+def test_encoding_round_trips_every_finite_code():
+    codes = np.r_[np.arange(127), np.arange(129, 255)]  # -0 (128) encodes as +0
+    np.testing.assert_array_equal(W.e4m3_encode(orc.e4m3_decode(codes)), codes)
+
+
+def test_encoding_rounds_to_nearest_with_ties_to_even():
+    # midpoints between neighbouring codes go to the even code
+    vals = orc.e4m3_decode(np.arange(127))
+    mid = (vals[:-1] + vals[1:]) / 2
+    codes = W.e4m3_encode(mid)
+    lo = np.arange(126)
+    np.testing.assert_array_equal(codes, np.where(lo % 2 == 0, lo, lo + 1))
+    # just off the midpoint goes to the nearer code
+    np.testing.assert_array_equal(W.e4m3_encode(mid * (1 - 1e-9)), lo)
+    np.testing.assert_array_equal(W.e4m3_encode(mid * (1 + 1e-9)), lo + 1)
+
+
+def test_encoding_saturates_and_keeps_sign():
+    assert W.e4m3_encode(np.array([1e6]))[0] == 0x7E
+    assert W.e4m3_encode(np.array([-1e6]))[0] == 0xFE
+    assert W.e4m3_encode(np.array([-0.5]))[0] == 0xB0
+
+
+def test_generated_fp8_inputs_use_the_full_range():
+    wl = W.Fp8Workload("t", B=1, H=2, S=64, D=64, seed=3)
+    inp = W.generate_fp8(wl)
+    for codes, scale in zip((inp.q8, inp.k8, inp.v8), inp.scales):
+        v = orc.e4m3_decode(codes)
+        assert np.abs(v).max() == 448.0           # amax maps to the largest code
+        assert np.all(np.isfinite(v)) and scale > 0
