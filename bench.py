@@ -101,19 +101,19 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, H, S, D = q.shape
+    # One workspace for both calls: the forward leaves the rotated q and k in it
+    # and the backward reuses them.
     ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                      device="cuda")
-    fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
-                      device="cuda")
     docs = None if inp.doc_offsets is None else torch.from_numpy(inp.doc_offsets).cuda()
     pos = neox.NEOX_POS_ALIBI if wl.alibi else neox.NEOX_POS_ROPE
     kw = dict(pos=pos, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
               softmax_scale=wl.softmax_scale, doc_offsets=docs)
 
     def step(ev):
-        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=fws, phase_events=ev[0:3], **kw)
+        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=ws, phase_events=ev[0:3], **kw)
         neox.neox_attn_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, workspace=ws,
-                              phase_events=ev[3:7], **kw)
+                              phase_events=ev[3:7], reuse_rotated_qk=True, **kw)
 
     warm_ev = make_events(torch, 7)
     for _ in range(args.warmup):
@@ -344,10 +344,9 @@ def main():
         "fwd_rope_qk": dict(bytes=2 * rows * wl.D * (el + 2)
                             if wl.rotary_dim > 0 and el == 2 else 0,
                             ms=kms["fwd_rope_qk"], bound="hbm"),
-        # preprocess: reads o, dO and lse, writes Delta and the row log-sum-exp term;
-        # with rotary it also reads q, k and writes the rotated bf16 copies
-        "bwd_pre": dict(bytes=2 * rows * wl.D * el + rows * 12
-                        + (rows * wl.D * (2 * el + 4) if wl.rotary_dim > 0 and el == 2 else 0),
+        # preprocess: reads o, dO and lse, writes Delta and the row log-sum-exp term
+        # (the rotated q and k are reused from the forward's workspace)
+        "bwd_pre": dict(bytes=2 * rows * wl.D * el + rows * 12,
                         ms=kms["bwd_pre"], bound="hbm"),
     }
     kern = {n: kd for n, kd in kern.items()

@@ -133,7 +133,7 @@ def _event_array(events):
 
 
 def _make_args(q, *, pos, rotary_dim, rope_base, alibi_slopes, causal, softmax_scale,
-               doc_offsets, out_f32, tensors, phase_events=None):
+               doc_offsets, out_f32, tensors, phase_events=None, reuse_rotated_qk=False):
     B, H, S, D = _shape(q)
     a = _lib.NeoxAttnArgs()
     a.B, a.H, a.S, a.D = B, H, S, D
@@ -148,6 +148,7 @@ def _make_args(q, *, pos, rotary_dim, rope_base, alibi_slopes, causal, softmax_s
         a.doc_offsets = doc_offsets.data_ptr()
         a.n_docs = int(doc_offsets.shape[1]) - 1
     a.out_dtype = NEOX_OUT_F32 if out_f32 else NEOX_OUT_SAME
+    a.reuse_rotated_qk = int(bool(reuse_rotated_qk))
     strides = (_lib.NeoxStrides * 8)()
     for n, t in enumerate(tensors):
         if t is not None:
@@ -186,14 +187,16 @@ def neox_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, *, pos: int = NEOX_POS_R
                      rotary_dim: int = 0, rope_base: float = 10000.0, alibi_slopes=None,
                      causal: bool = True, softmax_scale: Optional[float] = None,
                      doc_offsets=None, out_f32: bool = False, workspace=None,
-                     phase_events=None, stream=None) -> None:
+                     phase_events=None, reuse_rotated_qk: bool = False, stream=None) -> None:
     """Calls neox_attn_bwd_ex; strides are taken from the tensors.  ``phase_events``
     is None or 4 events (before/after the preprocess, after the main kernel,
-    after the dq finalize)."""
+    after the dq finalize).  ``reuse_rotated_qk``: the workspace was the
+    forward's workspace and still holds the rotated q and k."""
     a, keep = _make_args(q, pos=pos, rotary_dim=rotary_dim, rope_base=rope_base,
                          alibi_slopes=alibi_slopes, causal=causal, softmax_scale=softmax_scale,
                          doc_offsets=doc_offsets, out_f32=out_f32,
-                         tensors=[q, k, v, o, dout, dq, dk, dv], phase_events=phase_events)
+                         tensors=[q, k, v, o, dout, dq, dk, dv], phase_events=phase_events,
+                         reuse_rotated_qk=reuse_rotated_qk)
     nbytes = _nbytes(workspace)
     st = _lib.load().neox_attn_bwd_ex(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                       _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),

@@ -46,6 +46,7 @@ class NeoxAttnArgs(ctypes.Structure):
         ("doc_offsets", c_void_p), ("n_docs", c_int), ("out_dtype", c_int),
         ("strides", ctypes.POINTER(NeoxStrides)),
         ("phase_events", ctypes.POINTER(c_void_p)),
+        ("reuse_rotated_qk", c_int),
     ]
 
 

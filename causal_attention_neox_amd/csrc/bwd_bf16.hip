@@ -9,7 +9,8 @@
 //   prep:  per row, Delta_i = dO_i . o_i, nlse_i = -lse_i log2(e) (with the
 //          ALiBi row term folded in), and the rotated rows q~ = R q, k~ = R k
 //          written once to the workspace (NeoX rotate-half, "FasterTransformer
-//          GPT-NeoX 推理指南"), so the other passes never rotate.
+//          GPT-NeoX 推理指南"), so the other passes never rotate; when the
+//          forward already left q~ and k~ in that workspace they are kept.
 //   dK/dV: one workgroup per (batch, head, 128 keys), K-stationary; 64-row
 //          q-tiles stream through LDS:
 //            S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
                                          (int64_t)i * p.so.s + d0);
     gw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h +
                                          (int64_t)i * p.sdo.s + d0);
-    if (rd > 0) {
+    if (rd > 0 && !p.qk_ready) {
       qw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
                                            (int64_t)i * p.sq.s + d0);
       kw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       p.nlse[r] = nl;
     }
   }
-  if (rd == 0) return;
+  if (rd == 0 || p.qk_ready) return;  // no rotation, or q~ and k~ already in place
 
   if (act) {
     *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][0][d0]) = qw;

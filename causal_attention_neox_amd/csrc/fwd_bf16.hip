@@ -22,9 +22,11 @@
 //    conflicts; only the rotary dims of K pass through registers.  Two LDS
 //    buffers, one barrier per tile; every LDS operand address is a per-lane
 //    register (moved by one tile when the buffers swap) plus an immediate.
-//  * Tiles fully inside every row's allowed range skip the mask; the running
-//    max is raised lazily (only when a row's max grows by more than 2^8 in the
-//    exp2 domain), so O and the row sum are rescaled rarely.
+//  * Tiles fully inside every row's allowed range skip the mask.  A tile's
+//    probabilities are taken against the running max without first finding
+//    the tile's own max; their per-lane sum bounds each of them, and only a
+//    tile whose sum exceeds 2^8 (or a row's first tile) finds the max, raises
+//    the running max and rescales O and the row sum.
 //  * Workgroups are issued heaviest q-tile first, heads fastest: with B*H a
 //    multiple of 8 all q-tiles of a head share one XCD and its L2.  (Grouping
 //    each XCD's heads so that their K/V stay L2-resident cuts the fetched
@@ -43,7 +45,9 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// A lane's probabilities over one tile (its 32 keys) may sum to at most 2^8
+// before the exact path raises the running max, so each stays <= 2^8.
+constexpr float kTileSumLimit = 256.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -324,30 +328,51 @@ struct FwdState {
             if (ko < jlo || ko > jhi) sacc[blk][r] = -INFINITY;
           }
       }
-      float mx = fmaxf(sacc[0][0], fmaxf(sacc[0][1], sacc[0][2]));
+      // Probabilities against the current running max, straight into the
+      // packed bf16 B operands; the raw scores stay in sacc.  The tile's row
+      // max is only needed when some probability could exceed 2^8: this
+      // lane's sum over its 32 keys bounds every one of them, so a sum above
+      // 2^8 (or a row without a reference yet) takes the exact path, which
+      // raises the running max to the tile max, rescales O and the row sum
+      // and exponentiates again.
+      elem8 pb[BN / 16];
+      float ts = 0.0f;
+      auto expo = [&](float mref) {
+        ts = 0.0f;
 #pragma unroll
-      for (int i = 3; i < 31; i += 2)
-        mx = fmaxf(mx, fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
-      mx = fmaxf(mx, sacc[1][15]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = ALIBI ? mx : mx * c2;  // tile max in the exp2 domain
-      if (__any(mt > m_ref + kRescaleThreshold)) {
+        for (int cp = 0; cp < BN / 16; ++cp) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = sacc[cp >> 1][8 * (cp & 1) + e];
+            pv[e] = ALIBI ? fast_exp2(x - mref) : fast_exp2(__builtin_fmaf(x, c2, -mref));
+            ts += pv[e];
+          }
+          pb[cp] = pack8(pv);
+        }
+      };
+      bool exact = __any(m_ref == -INFINITY);
+      if (!exact) {
+        expo(m_ref);
+        exact = __any(ts > kTileSumLimit);
+      }
+      if (exact) {
+        float mx = fmaxf(sacc[0][0], fmaxf(sacc[0][1], sacc[0][2]));
+#pragma unroll
+        for (int i = 3; i < 31; i += 2)
+          mx = fmaxf(mx, fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
+        mx = fmaxf(mx, sacc[1][15]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = ALIBI ? mx : mx * c2;  // tile max in the exp2 domain
         const float m_new = fmaxf(m_ref, mt);
         const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         m_ref = m_new;
+        expo(m_ref == -INFINITY ? 0.0f : m_ref);
       }
-      const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = sacc[blk][r];
-          sacc[blk][r] = ALIBI ? fast_exp2(x - m_use) : fast_exp2(__builtin_fmaf(x, c2, -m_use));
-          l_run += sacc[blk][r];
-        }
+      l_run += ts;
       // V^T operands are read one MFMA ahead of their use.
       constexpr int NDB = D / 32, NG = (BN / 16) * NDB;
       auto vread = [&](int g) {
@@ -356,14 +381,6 @@ struct FwdState {
         const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
         return __builtin_bit_cast(elem8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      elem8 pb[BN / 16];
-#pragma unroll
-      for (int cp = 0; cp < BN / 16; ++cp) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = sacc[cp >> 1][8 * (cp & 1) + e];
-        pb[cp] = pack8(pv);
-      }
       elem8 vcur = vread(0);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {

@@ -57,6 +57,7 @@ struct BwdParams {
   uint16_t* krot;  // [B][H][S][D] 16-bit workspace: rotated k
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int out_f32;     // dq, dk, dv stored as fp32
+  int qk_ready;    // qrot / krot already hold R q and R k (written by the forward)
 };
 
 // One decoding step: the new token of every (batch, head) against its cache.

@@ -115,6 +115,7 @@ int validate_common(const neox_attn_args* a) {
     return NEOX_E_ARG;
   }
   if (a->alibi_slopes && a->pos != NEOX_POS_ALIBI) return NEOX_E_ARG;
+  if (a->reuse_rotated_qk != 0 && a->reuse_rotated_qk != 1) return NEOX_E_ARG;
   if (a->doc_offsets) {
     if (a->n_docs < 1 || a->n_docs > (1 << 24)) return NEOX_E_ARG;
     if ((reinterpret_cast<uintptr_t>(a->doc_offsets) & 3u) != 0) return NEOX_E_ALIGN;
@@ -168,9 +169,10 @@ int prepare_rope(const neox_attn_args* a, int dev, hipStream_t st, const float2*
   return NEOX_OK;
 }
 
-// Backward workspace: fp32 dq accumulator [rows][D], fp32 Delta [rows], fp32
-// -lse*log2e [rows], and the rotated bf16 q and k [rows][D] each; 256-byte
-// aligned pieces, rows = B*H*S.
+// Backward workspace: the rotated 16-bit q and k [rows][D] each (first, at the
+// offsets the forward workspace uses, so one buffer can serve both calls), the
+// fp32 dq accumulator [rows][D], fp32 Delta [rows] and fp32 -lse*log2e [rows];
+// 256-byte aligned pieces, rows = B*H*S.
 struct BwdWorkspace {
   size_t dq_acc, delta, nlse, qrot, krot, total;
 };
@@ -180,16 +182,16 @@ bool bwd_workspace_layout(int B, int H, int S, int D, BwdWorkspace* w) {
   const int64_t rows = (int64_t)B * H * S;
   if (rows >= kMaxRows || D > 4096) return false;
   size_t off = 0;
+  w->qrot = off;
+  off += round256((size_t)rows * (size_t)D * 2u);
+  w->krot = off;
+  off += round256((size_t)rows * (size_t)D * 2u);
   w->dq_acc = off;
   off += round256((size_t)rows * (size_t)D * 4u);
   w->delta = off;
   off += round256((size_t)rows * 4u);
   w->nlse = off;
   off += round256((size_t)rows * 4u);
-  w->qrot = off;
-  off += round256((size_t)rows * (size_t)D * 2u);
-  w->krot = off;
-  off += round256((size_t)rows * (size_t)D * 2u);
   w->total = off;
   return true;
 }
@@ -349,6 +351,8 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   p.sdq = to_internal(s ? s[5] : def);
   p.sdk = to_internal(s ? s[6] : def);
   p.sdv = to_internal(s ? s[7] : def);
+  p.qk_ready = (a->reuse_rotated_qk && a->dtype != NEOX_F32 && a->pos == NEOX_POS_ROPE &&
+                a->rotary_dim > 0) ? 1 : 0;
   p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
   const hipError_t e = a->dtype == NEOX_BF16  ? neox::launch_bwd_bf16(p, hs, ev)

@@ -114,6 +114,13 @@ typedef struct neox_strides {
  *                preprocess kernel, [1] after it, [2] after the dK/dV kernel
  *                and [3] at its end (after the dQ kernel, or the fp32 path's
  *                dq finalize).  The events are owned by the caller.
+ *  reuse_rotated_qk  0 or 1, backward only (16-bit storage with rotary_dim > 0;
+ *                ignored otherwise).  1 promises that the backward workspace
+ *                already holds the rotated rows q~ and k~ because it was passed
+ *                as the workspace of the forward call with the same q, k and
+ *                rotary arguments and nothing wrote to it since; the backward
+ *                then skips recomputing them (saving a read of q, k and a
+ *                write of q~, k~).  The results are bit-identical to 0.
  */
 typedef struct neox_attn_args {
   int B, H, S, D;
@@ -129,6 +136,7 @@ typedef struct neox_attn_args {
   int out_dtype;
   const neox_strides* strides;
   void* const* phase_events;
+  int reuse_rotated_qk;
 } neox_attn_args;
 
 /* Text of a status code (static storage, never NULL). */
@@ -164,11 +172,13 @@ int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace the backward needs, in five 256-byte aligned
- * parts: an fp32 [B, H, S, D] dq accumulator, two fp32 [B, H, S] row terms
- * (the softmax-gradient row sum and the negated base-2 log-sum-exp), and the
- * rotated q and k in the 16-bit storage type, [B, H, S, D] each (used by the
- * bf16 and fp16 paths only; the size does not depend on dtype) -- B*H*S*(8D + 8)
- * bytes up to rounding, linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
+ * parts: the rotated q and k in the 16-bit storage type, [B, H, S, D] each
+ * (used by the bf16 and fp16 paths only; placed first, exactly where the
+ * forward workspace holds them, so a backward workspace also serves as the
+ * forward's -- see reuse_rotated_qk), an fp32 [B, H, S, D] dq accumulator (fp32
+ * path) and two fp32 [B, H, S] row terms (the softmax-gradient row sum and the
+ * negated base-2 log-sum-exp); the size does not depend on dtype --
+ * B*H*S*(8D + 8) bytes up to rounding, linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
 size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
 
 /*

@@ -36,9 +36,11 @@ def to_f64(t) -> np.ndarray:
 
 
 def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force_ex: bool = False,
-                fwd_workspace: bool = True):
+                fwd_workspace: bool = True, reuse_qk: bool = False):
     """Forward (and backward) on the GPU through the C ABI; returns torch tensors.
-    ``fwd_workspace`` gives the forward its optional workspace (pre-rotated queries and keys)."""
+    ``fwd_workspace`` gives the forward its optional workspace (pre-rotated queries and keys);
+    ``reuse_qk`` runs the forward in the backward's workspace and lets the backward
+    reuse the rotated rows it leaves there."""
     torch = torch_mod()
     wl = inp.wl
     q, k, v = (to_device(inp, n) for n in ("q", "k", "v"))
@@ -52,7 +54,12 @@ def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force
               softmax_scale=wl.softmax_scale, doc_offsets=docs, out_f32=out_f32)
     B, H, S, D = q.shape
     fws = None
-    if fwd_workspace:
+    ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                     device="cuda")
+    if reuse_qk:
+        use_ex = True
+        fws = ws
+    elif fwd_workspace:
         fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                           device="cuda")
     if use_ex:
@@ -65,10 +72,9 @@ def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force
         do = to_device(inp, "dout")
         o_in = o if o.dtype == q.dtype else o.to(q.dtype)
         dq, dk, dv = (torch.empty(q.shape, dtype=odt, device="cuda") for _ in range(3))
-        ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
-                         device="cuda")
         if use_ex:
-            neox.neox_attn_bwd_ex(q, k, v, o_in, do, lse, dq, dk, dv, workspace=ws, **kw)
+            neox.neox_attn_bwd_ex(q, k, v, o_in, do, lse, dq, dk, dv, workspace=ws,
+                                  reuse_rotated_qk=reuse_qk, **kw)
         else:
             neox.neox_rope_attn_bwd(q, k, v, o_in, do, lse, dq, dk, dv, wl.rotary_dim,
                                     wl.rope_base, wl.causal, wl.softmax_scale, workspace=ws)

@@ -139,6 +139,7 @@ def make_args(**kw):
     (dict(n_docs=3), E_ARG),                      # n_docs without offsets
     (dict(doc_offsets=0x1000, n_docs=0), E_ARG),
     (dict(doc_offsets=0x1002, n_docs=2), E_ALIGN),
+    (dict(reuse_rotated_qk=2), E_ARG),
 ])
 def test_ex_validation(lib, kw, status):
     a = make_args(**kw)
@@ -182,7 +183,7 @@ def test_workspace_size_is_linear_in_sequence_length(lib):
     for (B, H, D) in [(1, 1, 64), (4, 64, 96), (1, 32, 128)]:
         for S in (1, 17, 2048, 16384, 1 << 20):
             rows = B * H * S
-            expect = r256(rows * D * 4) + 2 * r256(rows * 4) + 2 * r256(rows * D * 2)
+            expect = 2 * r256(rows * D * 2) + r256(rows * D * 4) + 2 * r256(rows * 4)
             assert lib.neox_rope_attn_bwd_workspace_size(B, H, S, D) == expect
     assert lib.neox_rope_attn_bwd_workspace_size(0, 1, 1, 64) == 0
     assert lib.neox_rope_attn_bwd_workspace_size(1 << 16, 1 << 8, 1 << 8, 64) == 0

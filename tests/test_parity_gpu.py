@@ -190,6 +190,21 @@ def test_forward_is_deterministic_and_writes_every_element(gpu):
         assert torch.equal(lse, outs[0][1])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_reusing_the_forward_rotation_is_bit_identical(gpu, dtype):
+    """One workspace for both calls: the forward leaves q~ and k~ in it and the
+    backward skips its own rotation; every output must be bit-identical to the
+    run with separate workspaces (both passes rotate with the same arithmetic)."""
+    wl = pu.small_workload(2, 3, 257, 96, 24, dtype=dtype, seed=23)
+    inp = generate(wl)
+    ref = pu.run_library(inp, backward=True, force_ex=True)
+    got = pu.run_library(inp, backward=True, reuse_qk=True)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert gpu.equal(got[name], ref[name]), name
+    heads = [(b, h) for b in range(2) for h in range(3)]
+    pu.compare(got, pu.oracle_heads(inp, heads), heads, dtype, label=f"reuse {dtype}")
+
+
 def test_backward_is_deterministic(gpu):
     """The bf16 backward reduces every gradient inside one workgroup in a
     fixed order (no atomics), so repeated calls agree bit for bit."""
