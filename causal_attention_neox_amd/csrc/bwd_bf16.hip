@@ -161,6 +161,62 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Row terms only (no rotation to do: rotary off, or q~ and k~ already in the
+// workspace): Delta_i = dO_i . o_i and nlse_i.  Each wave takes NR row groups
+// and issues all their loads before the first use, so more bytes are in
+// flight per wave than in the rotating pass.
+constexpr int kDeltaRows = 4;  // row groups per wave
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  using RG = RowGroups<D>;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW, NR = kDeltaRows;
+  const AttnShape& a = p.a;
+  const int S = a.S;
+  const int rows = a.B * a.H * S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane & (G - 1), rw = lane / G;
+  const int wrow0 = (blockIdx.x * 4 + wave) * RPW * NR;
+  if (wrow0 >= rows) return;  // whole waves only
+  const int d0 = 8 * g;
+  u32x4 ow[NR], gw[NR];
+  float lse[NR];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int r = wrow0 + n * RPW + rw;
+    ow[n] = gw[n] = u32x4{0u, 0u, 0u, 0u};
+    lse[n] = 0.0f;
+    if (r < rows && g < C) {
+      const int bh = r / S, i = r - bh * S;
+      const int b = bh / a.H, h = bh - b * a.H;
+      ow[n] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b + h * p.so.h +
+                                              (int64_t)i * p.so.s + d0);
+      gw[n] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b +
+                                              h * p.sdo.h + (int64_t)i * p.sdo.s + d0);
+      if (g == 0) lse[n] = p.lse[r];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum = fmaf(el_lo(ow[n][e]), el_lo(gw[n][e]), sum);
+      sum = fmaf(el_hi(ow[n][e]), el_hi(gw[n][e]), sum);
+    }
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+    const int r = wrow0 + n * RPW + rw;
+    if (g == 0 && r < rows) {
+      const int bh = r / S, i = r - bh * S;
+      p.delta[r] = sum;
+      float nl = -lse[n] * kLog2e;
+      if (a.alibi) nl -= alibi_slope_log2(a, bh % a.H) * (float)i;
+      p.nlse[r] = nl;
+    }
+  }
+}
+
 // ------------------------------------------------------------------- dK / dV
 
 // Eight waves, two per SIMD.  Wave w owns the 32 keys 32 (w & 3) .. +31 of
@@ -877,7 +933,14 @@ template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
   if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
+  if (p.a.rd == 0 || p.qk_ready) {
+    const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+    const int per_block = kDeltaRows * RowGroups<D>::RPB;
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
+                       dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
   const unsigned BH = (unsigned)(p.a.B * p.a.H);
