@@ -16,10 +16,11 @@
 //    V is transposed on its way into LDS (4 x 4 byte blocks through v_perm)
 //    into rows of one dim with the keys in exactly that order, so the A
 //    operand of O^T += V^T P^T is two 16-byte reads.
-//  * P is stored as 2^4 P in E4M3 (round to nearest even): the running max is
-//    raised lazily, only when a row's max grows by more than 2^4, so
-//    2^4 P <= 2^8 stays inside E4M3's range (448), and the same 2^4 cancels
-//    between O and the row sum.
+//  * P is stored as 2^4 P in E4M3 (round to nearest even), taken against the
+//    running max; a lane's tile sum above 2^8 (checked before use) raises the
+//    max first (D = 128: the tile max is found every tile and the running max
+//    raised when it grows by more than 2^4), so every 2^4 P <= 2^8 stays inside
+//    E4M3's range (448), and the same 2^4 cancels between O and the row sum.
 //  * Rows are padded by 16 bytes (K: D + 16, V^T: 64 + 16) so that the 16-byte
 //    operand reads of 8 consecutive lanes fall on distinct banks.  The next
 //    tile is loaded into registers while the current one is used, then
@@ -35,7 +36,7 @@ constexpr int F8_BM = 128;           // queries per workgroup
 constexpr int F8_BN = 64;            // keys per tile
 constexpr int F8_NT = 256;           // threads per workgroup
 constexpr float kPShift = 4.0f;      // P stored as 2^4 P
-constexpr float kF8Lazy = 4.0f;      // running-max raise threshold (log2 units)
+constexpr float kF8SumLimit = 256.0f;  // a lane's tile sum of 2^4 P before the max is raised
 
 template <int D>
 struct F8Tile {
@@ -202,28 +203,63 @@ __global__ __launch_bounds__(F8_NT, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
         const float x = sacc[kb2][r] * c2;
         s[16 * kb2 + r] = (full || key <= hi) ? x : -INFINITY;
       }
-    float mx = s[0];
+    // 2^4 P in E4M3, four per dword, in the score registers' key order, taken
+    // against the running max without finding the tile max first.  This lane's
+    // sum over its 32 keys bounds each value: a sum above 2^8 (or a row
+    // without a reference yet) takes the exact path, which raises the running
+    // max to the tile max, rescales O and the row sum and converts again, so
+    // every stored 2^4 P stays <= 2^8 (E4M3 reaches 448).
+    i32x8 pop;
+    float ts = 0.0f;
+    auto expo = [&](float mref) {
+      const float mo = mref - kPShift;
+      ts = 0.0f;
 #pragma unroll
-    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, s[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half holds the row's other keys
-    if (mx > m + kF8Lazy) {               // raise the running max (rarely after the first tile)
-      const float corr = fast_exp2(m - mx);
+      for (int w = 0; w < 8; ++w) {
+        const float p0 = fast_exp2(s[4 * w] - mo), p1 = fast_exp2(s[4 * w + 1] - mo);
+        const float p2 = fast_exp2(s[4 * w + 2] - mo), p3 = fast_exp2(s[4 * w + 3] - mo);
+        ts += (p0 + p1) + (p2 + p3);
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, d, true);
+        pop[w] = d;
+      }
+    };
+    if constexpr (D > 96) {
+      // D = 128: the two paths do not fit the register budget; find the tile
+      // max every tile and raise the running max lazily (by more than 2^4).
+      float mx = s[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) mx = fmaxf(mx, s[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (mx > m + kPShift) {
+        const float corr = fast_exp2(m - mx);
+        l *= corr;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+        m = mx;
+      }
+      expo(m);
+      l += ts;
+    } else {
+    bool exact = __any(m == -INFINITY);
+    if (!exact) {
+      expo(m);
+      exact = __any(ts > kF8SumLimit);
+    }
+    if (exact) {
+      float mx = s[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) mx = fmaxf(mx, s[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half holds the row's other keys
+      const float m_new = fmaxf(m, mx);
+      const float corr = m_new == -INFINITY ? 1.0f : fast_exp2(m - m_new);
       l *= corr;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
-      m = mx;
+      m = m_new;
+      expo(m == -INFINITY ? 0.0f : m);
     }
-    // 2^4 P in E4M3, four per dword, in the score registers' key order.
-    const float mo = m - kPShift;
-    i32x8 pop;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float p0 = fast_exp2(s[4 * w] - mo), p1 = fast_exp2(s[4 * w + 1] - mo);
-      const float p2 = fast_exp2(s[4 * w + 2] - mo), p3 = fast_exp2(s[4 * w + 3] - mo);
-      l += (p0 + p1) + (p2 + p3);
-      int d = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-      d = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, d, true);
-      pop[w] = d;
+    l += ts;
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
