@@ -502,6 +502,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const Ops tn = g + 1 < NG ? tops(g + 1) : tc;
+      __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
       dvacc[g % NB] = mfma32x32x16(tc.g, pb[g / NB], dvacc[g % NB]);
       dkacc[g % NB] = mfma32x32x16(tc.q, sb[g / NB], dkacc[g % NB]);
       tc = tn;
@@ -745,6 +746,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
       for (int c = 0; c < D / 16; ++c) {
         elem8 kn = kc_, vn = vc_;
         if (c + 1 < D / 16) rows(c + 1, kn, vn);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
         sacc = mfma32x32x16(kc_, qreg[c], sacc);
         dpacc = mfma32x32x16(vc_, greg[c], dpacc);
         kc_ = kn;
@@ -788,6 +790,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const elem8 kn = g + 1 < NG ? kt_op(g + 1) : ka;
+        __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
         dqacc[g % NB] = mfma32x32x16(ka, sb[g / NB], dqacc[g % NB]);
         ka = kn;
       }

@@ -301,6 +301,7 @@ struct FwdState {
           k0n = lds_read8(lds + kaddr[c + 1]);
           k1n = lds_read8(lds + kaddr[c + 1] + 32 * D);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
         sacc[0] = mfma32x32x16(k0c, qreg[c], sacc[0]);
         sacc[1] = mfma32x32x16(k1c, qreg[c], sacc[1]);
         k0c = k0n;
@@ -385,6 +386,7 @@ struct FwdState {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const elem8 vnext = g + 1 < NG ? vread(g + 1) : vcur;
+        __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
         oacc[g % NDB] = mfma32x32x16(vcur, pb[g / NDB], oacc[g % NDB]);
         vcur = vnext;
       }
