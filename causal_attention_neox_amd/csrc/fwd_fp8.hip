@@ -174,17 +174,27 @@ __global__ __launch_bounds__(F8_NT, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
     const uint8_t* buf = lds + (t & 1) * T::BUF;
     const int k0 = t * F8_BN;
 
-    f32x16 sacc[2];
+    // K~ operands (key block kb2, 64-dim step c), read one MFMA ahead (D <= 96).
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    auto kread = [&](int i) {
+      const int kb2 = i / T::NC, c = i % T::NC;
+      const int d0 = 64 * c + 32 * hh;
+      return d0 < D ? lds_read32(buf + (kb2 * 32 + ql) * T::KS + d0)
+                    : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    };
+    if constexpr (D <= 96) {
+      i32x8 kcur = kread(0);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < T::NC; ++c) {
-        const int d0 = 64 * c + 32 * hh;
-        const i32x8 kop = d0 < D ? lds_read32(buf + (kb2 * 32 + ql) * T::KS + d0)
-                                 : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        sacc[kb2] = mfma_f8(kop, qop[c], sacc[kb2]);
+      for (int i = 0; i < 2 * T::NC; ++i) {
+        const i32x8 knext = i + 1 < 2 * T::NC ? kread(i + 1) : kcur;
+        __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this MFMA
+        sacc[i / T::NC] = mfma_f8(kcur, qop[i % T::NC], sacc[i / T::NC]);
+        kcur = knext;
       }
+    } else {  // D = 128: no registers to spare for reading ahead
+#pragma unroll
+      for (int i = 0; i < 2 * T::NC; ++i)
+        sacc[i / T::NC] = mfma_f8(kread(i), qop[i % T::NC], sacc[i / T::NC]);
     }
     // Next tile into the other buffer (its readers finished before this barrier).
     if (t + 1 < kt_hi) {
@@ -261,10 +271,21 @@ __global__ __launch_bounds__(F8_NT, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
     }
     l += ts;
     }
+    auto vread = [&](int db) {
+      return lds_read32(buf + T::KBYTES + (db * 32 + ql) * T::VS + 32 * hh);
+    };
+    if constexpr (D <= 96) {
+      i32x8 vcur = vread(0);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const i32x8 vop = lds_read32(buf + T::KBYTES + (db * 32 + ql) * T::VS + 32 * hh);
-      oacc[db] = mfma_f8(vop, pop, oacc[db]);
+      for (int db = 0; db < D / 32; ++db) {
+        const i32x8 vnext = db + 1 < D / 32 ? vread(db + 1) : vcur;
+        __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this MFMA
+        oacc[db] = mfma_f8(vcur, pop, oacc[db]);
+        vcur = vnext;
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_f8(vread(db), pop, oacc[db]);
     }
   }
 
