@@ -222,16 +222,18 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // Eight waves, two per SIMD.  Wave w owns the 32 keys 32 (w & 3) .. +31 of
 // the workgroup's 128 and query half w >> 2 (32 rows) of every 64-row q-tile;
 // the two waves of a key group add their dV / dK~ partial sums in the
-// epilogue.  K~ and V are the B operands of S and dP: held in registers where
-// they fit (D = 64), else re-read from stationary LDS tiles.
+// epilogue.  K~ and V are the B operands of S and dP: K~ held in registers up
+// to D = 96 and V at D = 64 (where they fit), else re-read from stationary LDS
+// tiles.
 template <int D>
 struct DkdvLds {
   static constexpr int BMQ = 64;
   static constexpr int C = D / 8;
-  static constexpr bool kRegKV = D <= 64;        // K~ and V B operands held in registers
-  static constexpr int KT = 0;                   // K~ [BNK][D]
+  static constexpr bool kRegK = D <= 96;         // K~ B operands held in registers
+  static constexpr bool kRegV = D <= 64;         // V B operands held in registers
+  static constexpr int KT = 0;                   // K~ [BNK][D] (staging for the registers)
   static constexpr int VT = KT + BNK * D;        // V [BNK][D] (when not in registers)
-  static constexpr int Q0 = VT + (kRegKV ? 0 : BNK * D);  // Q~ tiles [BMQ][D] x2
+  static constexpr int Q0 = VT + (kRegV ? 0 : BNK * D);  // Q~ tiles [BMQ][D] x2
   static constexpr int G0 = Q0 + 2 * BMQ * D;    // dO tiles x2
   static constexpr int F0 = G0 + 2 * BMQ * D;    // floats: nlse x2, Delta x2 (BMQ each)
   static constexpr int N16 = F0 + 2 * 4 * BMQ;   // total in uint16 units
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NB = D / 32;
   constexpr int NFB = 2 * C / 8;  // 1 KB direct-load blocks per wave (per tile / stationary pair)
   static_assert((2 * C) % 8 == 0, "tile blocks must split evenly over 8 waves");
-  constexpr bool kRegKV = L::kRegKV;
+  constexpr bool kRegK = L::kRegK, kRegV = L::kRegV;
   __shared__ __attribute__((aligned(16))) uint16_t lds[L::N16];
   float* fl = reinterpret_cast<float*>(lds + L::F0);  // nlse[2][BMQ], delta[2][BMQ]
 
@@ -358,11 +360,11 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int row = P / C, ch = (P % C) ^ swz<C>(row);
     const int rr = min(k0 + row, S - 1);
     load_lds16(kb + (int64_t)rr * kstr + 8 * ch, lds + L::KT + 512 * blk);
-    if constexpr (!kRegKV) load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, lds + L::VT + 512 * blk);
+    if constexpr (!kRegV) load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, lds + L::VT + 512 * blk);
   }
   fetch_q(qt_lo, lds + L::Q0, fl);
-  elem8 kreg[kRegKV ? D / 16 : 1], vreg[kRegKV ? D / 16 : 1];
-  if constexpr (kRegKV) {
+  elem8 kreg[kRegK ? D / 16 : 1], vreg[kRegV ? D / 16 : 1];
+  if constexpr (kRegV) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       vreg[c] = __builtin_bit_cast(elem8, u32x4{0u, 0u, 0u, 0u});
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (kRegKV) {
+  if constexpr (kRegK) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       kreg[c] = lds_read8(lds + L::KT + 8 * tpos<C>(32 * kg + ql, 2 * c + hh));
@@ -430,18 +432,16 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       Ops o;
       o.q = lds_read8(Qt + off);
       o.g = lds_read8(Gt + off);
-      if constexpr (!kRegKV) {
-        o.k = lds_read8(KTp + off + kq_delta);
-        o.v = lds_read8(VTp + off + kq_delta);
-      }
+      if constexpr (!kRegK) o.k = lds_read8(KTp + off + kq_delta);
+      if constexpr (!kRegV) o.v = lds_read8(VTp + off + kq_delta);
       return o;
     };
     Ops cur = ops(0);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       const Ops nxt = c + 1 < D / 16 ? ops(c + 1) : cur;
-      sacc = mfma32x32x16(cur.q, kRegKV ? kreg[kRegKV ? c : 0] : cur.k, sacc);
-      dpacc = mfma32x32x16(cur.g, kRegKV ? vreg[kRegKV ? c : 0] : cur.v, dpacc);
+      sacc = mfma32x32x16(cur.q, kRegK ? kreg[kRegK ? c : 0] : cur.k, sacc);
+      dpacc = mfma32x32x16(cur.g, kRegV ? vreg[kRegV ? c : 0] : cur.v, dpacc);
       cur = nxt;
     }
 
