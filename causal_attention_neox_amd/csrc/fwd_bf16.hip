@@ -21,7 +21,7 @@
 //    unpadded, XOR-swizzled layout that keeps the operand reads free of bank
 //    conflicts; only the rotary dims of K pass through registers.  Two LDS
 //    buffers, one barrier per tile; every LDS operand address is a per-lane
-//    register (moved by one tile when the buffers swap) plus an immediate.
+//    register offset from the buffer's base plus an immediate.
 //  * Tiles fully inside every row's allowed range skip the mask.  A tile's
 //    probabilities are taken against the running max without first finding
 //    the tile's own max; their per-lane sum bounds each of them, and only a
@@ -266,12 +266,11 @@ struct FwdState {
   elem8 qreg[D / 16];
   f32x16 oacc[D / 32];
   float m_ref, l_run;
-  // LDS element offsets (from lds) of this lane's operand reads in the current
-  // buffer; they move by +-TILE when the buffers swap.
+  // LDS element offsets of this lane's operand reads, from the start of a
+  // K or V tile buffer.
   int kaddr[D / 16];     // K~ A operand, rows 0..31 (per chunk pair); rows 32..63
                          // use the same swizzle, 32 * D elements further
   int vaddr[D / 32];     // V^T transposed reads (per dim block)
-  int bdelta;            // +TILE or -TILE: move to the other buffer
   int lo, hi, qi, hh, wave;
   float c2, sl2;
 
@@ -279,11 +278,20 @@ struct FwdState {
   // into the other buffer meanwhile.
   __device__ __forceinline__ void step(const FwdParams& p, const uint16_t* kb,
                                        const uint16_t* vb, int kt, int kt_hi, int buf) {
+    body(p, kb, vb, kt, kt_hi, lds + buf * TILE, lds + (2 + buf) * TILE, lds + (1 - buf) * TILE,
+         lds + (3 - buf) * TILE);
+  }
+  // The tile buffers come in as distinct restrict pointers, so the compiler
+  // knows the operand reads of this tile do not alias the direct-to-LDS loads
+  // of the next one still in flight (else every LDS read waits for them).
+  __device__ __forceinline__ void body(const FwdParams& p, const uint16_t* kb,
+                                       const uint16_t* vb, int kt, int kt_hi,
+                                       const uint16_t* __restrict__ Kc,
+                                       const uint16_t* __restrict__ Vc,
+                                       uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
     const AttnShape& a = p.a;
     const int S = a.S;
     const int k0 = kt * BN;
-    uint16_t* Kn = lds + (1 - buf) * TILE;
-    uint16_t* Vn = lds + (3 - buf) * TILE;
     const bool more = kt + 1 < kt_hi;
     if (more) tp.fetch(kb, p.sk.s, vb, p.sv.s, k0 + BN, S, a.rd, Kn, Vn, wave);
 
@@ -293,13 +301,13 @@ struct FwdState {
       const bool need_mask = !__all(lane_full);
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       // K~ operands are read one dims step ahead of the MFMAs using them.
-      elem8 k0c = lds_read8(lds + kaddr[0]), k1c = lds_read8(lds + kaddr[0] + 32 * D);
+      elem8 k0c = lds_read8(Kc + kaddr[0]), k1c = lds_read8(Kc + kaddr[0] + 32 * D);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         elem8 k0n = k0c, k1n = k1c;
         if (c + 1 < D / 16) {
-          k0n = lds_read8(lds + kaddr[c + 1]);
-          k1n = lds_read8(lds + kaddr[c + 1] + 32 * D);
+          k0n = lds_read8(Kc + kaddr[c + 1]);
+          k1n = lds_read8(Kc + kaddr[c + 1] + 32 * D);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
         sacc[0] = mfma32x32x16(k0c, qreg[c], sacc[0]);
@@ -377,7 +385,7 @@ struct FwdState {
       // V^T operands are read one MFMA ahead of their use.
       constexpr int NDB = D / 32, NG = (BN / 16) * NDB;
       auto vread = [&](int g) {
-        const uint16_t* vp = lds + vaddr[g % NDB] + 16 * (g / NDB) * 8 * CPR;
+        const uint16_t* vp = Vc + vaddr[g % NDB] + 16 * (g / NDB) * 8 * CPR;
         const s16x4 v0 = lds_read_tr4(vp);
         const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
         return __builtin_bit_cast(elem8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -392,11 +400,6 @@ struct FwdState {
       }
     }
     if (more) tp.store(Kn, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) kaddr[c] += bdelta;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) vaddr[db] += bdelta;
-    bdelta = -bdelta;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -496,7 +499,6 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
   // (j&3)/2, half (j&1)) of key 16 cp + 4 hh + j/4 (+8).
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) st.kaddr[c] = 8 * (ql * CPR + ((2 * c + hh) ^ Swz<D>::k(ql)));
-  st.bdelta = TILE;
   {
     const int g16 = lane >> 4, j16 = lane & 15;
     const int vkey = 4 * hh + (j16 >> 2);
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
     const int vch = 2 * (g16 & 1) + ((j16 & 3) >> 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      st.vaddr[db] = 2 * TILE + 8 * (vkey * CPR + ((4 * db + vch) ^ vsw)) + 4 * (j16 & 1);
+      st.vaddr[db] = 8 * (vkey * CPR + ((4 * db + vch) ^ vsw)) + 4 * (j16 & 1);
   }
   st.tp.store(lds, kb, p.sk.s, kt_lo * BN, S, a.rd, a.rope);
   __builtin_amdgcn_s_waitcnt(0);
