@@ -850,82 +850,6 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ finalize
-
-// dq = R^T dQ~ (rotation by -theta), cast to the output type.  Row groups as
-// in the prep pass; rotary partners are exchanged through LDS.
-template <int D>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int out_f32,
-                                                          float dq_scale) {
-  using RG = RowGroups<D>;
-  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW;
-  __shared__ __attribute__((aligned(16))) float rowbuf[4][RPW][D];
-  const int S = p.a.S, rd = p.a.rd, half = rd >> 1;
-  const int rows = p.a.B * p.a.H * S;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane & (G - 1), rw = lane / G;
-  const int wrow0 = (blockIdx.x * 4 + wave) * RPW;
-  if (wrow0 >= rows) return;  // whole waves only
-  const int r = wrow0 + rw;
-  const bool act = r < rows && g < C;
-  const int bh = r / S, i = r - bh * S;
-  const int b = bh / p.a.H, h = bh - b * p.a.H;
-  const int d0 = 8 * g;
-  const bool rot_lane = act && d0 < rd;
-  f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
-  float2 cs[8];
-  if (act) {
-    const float* acc = p.dq_acc + (int64_t)r * D + d0;
-    lo = *reinterpret_cast<const f32x4*>(acc);
-    hi = *reinterpret_cast<const f32x4*>(acc + 4);
-  }
-  if (rot_lane) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d0 + e;
-      cs[e] = d < rd ? p.a.rope[(int64_t)i * half + (d < half ? d : d - half)]
-                     : float2{1.0f, 0.0f};
-    }
-  }
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lo[e] *= dq_scale;
-    hi[e] *= dq_scale;
-    x[e] = lo[e];
-    x[4 + e] = hi[e];
-  }
-  if (rd > 0) {
-    if (act) {
-      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0]) = lo;
-      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0 + 4]) = hi;
-    }
-    lds_wave_sync();
-    if (rot_lane) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        if (d < rd) {
-          const bool first = d < half;
-          const float xp = rowbuf[wave][rw][first ? d + half : d - half];
-          const float sn = first ? cs[e].y : -cs[e].y;  // transpose of rotate-half
-          x[e] = fmaf(xp, sn, x[e] * cs[e].x);
-        }
-      }
-    }
-  }
-  if (!act) return;
-  if (out_f32) {
-    float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-    *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
-  } else {
-    uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-    *reinterpret_cast<u32x4*>(orow) =
-        u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
-  }
-}
-
 template <int D>
 dim3 row_grid(const BwdParams& p) {
   const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
@@ -976,18 +900,5 @@ hipError_t NEOX_ELEM_FN(launch_bwd)(const BwdParams& p, hipStream_t st, const hi
   }
 }
 
-#if !NEOX_ELEM_F16  // one definition: the fp32 path's finalize (fp32 outputs)
-hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, float dq_scale) {
-  using namespace NEOX_ELEM_NS;
-  const dim3 blk(256);
-  switch (p.a.D) {
-    case 64: hipLaunchKernelGGL((dq_finalize_kernel<64>), row_grid<64>(p), blk, 0, st, p, out_f32, dq_scale); break;
-    case 96: hipLaunchKernelGGL((dq_finalize_kernel<96>), row_grid<96>(p), blk, 0, st, p, out_f32, dq_scale); break;
-    case 128: hipLaunchKernelGGL((dq_finalize_kernel<128>), row_grid<128>(p), blk, 0, st, p, out_f32, dq_scale); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-#endif
 
 }  // namespace neox

@@ -7,7 +7,7 @@
 //                applies R^T to dK~ in the epilogue.
 //   dq kernel:   one workgroup per (batch, head, 64 queries), 4 lanes per
 //                query, k-tiles of 32 rows in LDS; writes dQ~ to the
-//                workspace, and the shared finalize kernel applies R^T.
+//                workspace, and the finalize kernel applies R^T.
 // Delta_i = dO_i . o_i comes from the shared preprocess kernel.
 #include "device_common.hpp"
 
@@ -268,6 +268,79 @@ hipError_t launch_main(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// dq = R^T dQ~ (rotation by -theta) from the fp32 workspace accumulator.  Row
+// groups of G lanes, 16 B each; rotary partners are exchanged through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void dq_finalize_f32_kernel(BwdParams p) {
+  using RG = RowGroups<D>;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW;
+  __shared__ __attribute__((aligned(16))) float rowbuf[4][RPW][D];
+  const int S = p.a.S, rd = p.a.rd, half = rd >> 1;
+  const int rows = p.a.B * p.a.H * S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane & (G - 1), rw = lane / G;
+  const int wrow0 = (blockIdx.x * 4 + wave) * RPW;
+  if (wrow0 >= rows) return;  // whole waves only
+  const int r = wrow0 + rw;
+  const bool act = r < rows && g < C;
+  const int bh = r / S, i = r - bh * S;
+  const int b = bh / p.a.H, h = bh - b * p.a.H;
+  const int d0 = 8 * g;
+  const bool rot_lane = act && d0 < rd;
+  f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+  float2 cs[8];
+  if (act) {
+    const float* acc = p.dq_acc + (int64_t)r * D + d0;
+    lo = *reinterpret_cast<const f32x4*>(acc);
+    hi = *reinterpret_cast<const f32x4*>(acc + 4);
+  }
+  if (rot_lane) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
+      cs[e] = d < rd ? p.a.rope[(int64_t)i * half + (d < half ? d : d - half)]
+                     : float2{1.0f, 0.0f};
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = lo[e];
+    x[4 + e] = hi[e];
+  }
+  if (rd > 0) {
+    if (act) {
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0]) = lo;
+      *reinterpret_cast<f32x4*>(&rowbuf[wave][rw][d0 + 4]) = hi;
+    }
+    lds_wave_sync();
+    if (rot_lane) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + e;
+        if (d < rd) {
+          const bool first = d < half;
+          const float xp = rowbuf[wave][rw][first ? d + half : d - half];
+          const float sn = first ? cs[e].y : -cs[e].y;  // transpose of rotate-half
+          x[e] = fmaf(xp, sn, x[e] * cs[e].x);
+        }
+      }
+    }
+  }
+  if (!act) return;
+  float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+  *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+template <int D>
+hipError_t launch_finalize(const BwdParams& p, hipStream_t st) {
+  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
+  const dim3 grid((unsigned)((rows + RowGroups<D>::RPB - 1) / RowGroups<D>::RPB));
+  hipLaunchKernelGGL((dq_finalize_f32_kernel<D>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
@@ -290,7 +363,13 @@ hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* 
   }
   if (e != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  if ((e = launch_dq_finalize(p, st, 1, 1.0f)) != hipSuccess) return e;
+  switch (p.a.D) {
+    case 64: e = launch_finalize<64>(p, st); break;
+    case 96: e = launch_finalize<96>(p, st); break;
+    case 128: e = launch_finalize<128>(p, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
   return record_event(ev, 3, st);
 }
 

@@ -119,7 +119,6 @@ hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* 
 
 // dq = dq_scale * R^T dQ~ from the fp32 accumulator, cast; shared by both paths
 // (the bf16 path accumulates dS without the softmax scale and passes it here).
-hipError_t launch_dq_finalize(const BwdParams& p, hipStream_t st, int out_f32, float dq_scale);
 
 inline hipError_t record_event(const hipEvent_t* ev, int i, hipStream_t st) {
   return ev ? hipEventRecord(ev[i], st) : hipSuccess;
