@@ -225,6 +225,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // epilogue.  K~ and V are the B operands of S and dP: K~ held in registers up
 // to D = 96 and V at D = 64 (where they fit), else re-read from stationary LDS
 // tiles.
+constexpr int kDkdvPrefetch = 1;  // MFMA steps between an LDS operand's read and its use
+
 template <int D>
 struct DkdvLds {
   static constexpr int BMQ = 64;
@@ -236,7 +238,9 @@ struct DkdvLds {
   static constexpr int Q0 = VT + (kRegV ? 0 : BNK * D);  // Q~ tiles [BMQ][D] x2
   static constexpr int G0 = Q0 + 2 * BMQ * D;    // dO tiles x2
   static constexpr int F0 = G0 + 2 * BMQ * D;    // floats: nlse x2, Delta x2 (BMQ each)
-  static constexpr int N16 = F0 + 2 * 4 * BMQ;   // total in uint16 units
+  static constexpr int N16T = F0 + 2 * 4 * BMQ;  // tile-loop areas in uint16 units
+  static constexpr int EPI_BYTES = 2 * BNK * (D + 4) * 4;  // epilogue: dK~ and dV rows in fp32
+  static constexpr int N16 = N16T * 2 > EPI_BYTES ? N16T : EPI_BYTES / 2;  // LDS, uint16 units
   static_assert((F0 * 2) % 16 == 0, "float area alignment");
 };
 constexpr int NT8 = 512;
@@ -259,7 +263,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   int kt, bh;  // kt 0 (most queries) first; Q~ and dO of a head: 4 S D bytes
   xcd_order((S + BNK - 1) / BNK, BH, (int64_t)4 * S * D, kt, bh);
   const int b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int kg = wave & 3, qhalf = wave >> 2;
   const int ql = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -412,171 +417,275 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   // the compiler can tell the reads of this tile from the direct-to-LDS loads
   // of the next one still in flight (otherwise every LDS read would first
   // wait for all outstanding vector memory operations).
-  auto tile = [&](int qt, const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Gt,
+  auto tile = [&](auto masked, int qt, const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Gt,
                   uint16_t* __restrict__ Qn, const uint16_t* __restrict__ KTp,
                   const uint16_t* __restrict__ VTp, const float* __restrict__ Fc,
-                  float* __restrict__ Fn) {
+                  float* __restrict__ Fn) __attribute__((always_inline)) {
     const int q0 = qt * BMQ;
     const float* nlt = Fc + 32 * qhalf;
     const float* dlt = Fc + 2 * BMQ + 32 * qhalf;
     if (qt + 1 < qt_hi) fetch_q(qt + 1, Qn, Fn);
 
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    // Operands of dims step c: Q~ and dO rows (and K~ / V rows from LDS),
-    // read one step ahead of the MFMAs that use them.
-    struct Ops {
-      elem8 q, g, k, v;
-    };
-    auto ops = [&](int c) {
-      const int off = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
-      Ops o;
-      o.q = lds_read8(Qt + off);
-      o.g = lds_read8(Gt + off);
-      if constexpr (!kRegK) o.k = lds_read8(KTp + off + kq_delta);
-      if constexpr (!kRegV) o.v = lds_read8(VTp + off + kq_delta);
-      return o;
-    };
-    Ops cur = ops(0);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const Ops nxt = c + 1 < D / 16 ? ops(c + 1) : cur;
-      sacc = mfma32x32x16(cur.q, kRegK ? kreg[kRegK ? c : 0] : cur.k, sacc);
-      dpacc = mfma32x32x16(cur.g, kRegV ? vreg[kRegV ? c : 0] : cur.v, dpacc);
-      cur = nxt;
-    }
-
-    // P and dS' = P (dP - Delta) in place (the softmax scale is applied to
-    // dK~ at the end); register r is query q0 + 32 qhalf + 8 (r/4) + 4 hh + r%4.
-    // Tiles off the diagonal and the document edges take the unmasked copy.
     const int qw0 = q0 + 32 * qhalf;
-    const bool lane_full = (qw0 >= qlo) && (qw0 + 31 <= qhi);
-    auto pds = [&](auto masked) {
+
+    // The tile in four product groups, each MFMA independent of the VALU work
+    // placed beside it so that the two overlap:
+    //   S = Q~ K~^T;  dP = dO V^T beside P = exp2(S scale log2e + nlse);
+    //   dV^T += dO^T P beside dS' = P (dP - Delta);  dK~^T += Q~^T dS'.
+    // (The softmax scale is applied to dK~ at the end.)  Register r of S / dP
+    // is query q0 + 32 qhalf + 8 (r/4) + 4 hh + r%4.
+    {
       constexpr bool kMasked = decltype(masked)::value;
+      constexpr int NS = D / 16;  // dims steps of S and dP
       const int lo_off = qlo - qw0 - 4 * hh, hi_off = qhi - qw0 - 4 * hh;
+      auto roff = [&](int c) { return 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw)); };
+      // nlse of this lane's rows now; Delta is read during the last dP step.
+      f32x4 n4[4], d4[4];
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 n4 = *reinterpret_cast<const f32x4*>(nlt + 8 * a4 + 4 * hh);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + 8 * a4 + 4 * hh);
+      for (int a4 = 0; a4 < 4; ++a4) n4[a4] = *reinterpret_cast<const f32x4*>(nlt + 8 * a4 + 4 * hh);
+
+      // dO^T and Q~^T operands of (query chunk qc, dim block db): transposed
+      // reads.
+      constexpr int NG = 2 * NB;
+      auto top = [&](const uint16_t* T, int g) {
+        const int off = taddr[0][g % NB] + 16 * (g / NB) * D;
+        return tr8(T + off, taddr[1][g % NB] - taddr[0][g % NB]);
+      };
+      // One stream of MFMA steps: S (NS), dP (NS), dV (NG), dK (NG); each
+      // step's LDS operands are read PF steps ahead.
+      constexpr int NST = 2 * NS + 2 * NG;
+      constexpr int PF = kDkdvPrefetch;
+      struct Op {
+        elem8 a, b;
+      };
+      auto rd = [&](int t) {
+        Op o;
+        if (t < NS) {
+          o.a = lds_read8(Qt + roff(t));
+          o.b = kRegK ? o.a : lds_read8(KTp + roff(t) + kq_delta);
+        } else if (t < 2 * NS) {
+          o.a = lds_read8(Gt + roff(t - NS));
+          o.b = kRegV ? o.a : lds_read8(VTp + roff(t - NS) + kq_delta);
+        } else if (t < 2 * NS + NG) {
+          o.a = top(Gt, t - 2 * NS);
+          o.b = o.a;
+        } else {
+          o.a = top(Qt, t - 2 * NS - NG);
+          o.b = o.a;
+        }
+        return o;
+      };
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      u32x4 pw[2], sw[2];
+      Op ring[NST];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * a4 + e;
-          const float nl = ALIBI ? n4[e] + slj : n4[e];
-          float pr = fast_exp2(__builtin_fmaf(sacc[r], c2, nl));
-          if (kMasked) {
-            const int io = 8 * a4 + e;
-            if (io < lo_off || io > hi_off) pr = 0.0f;
+      for (int t = 0; t < PF; ++t) ring[t] = rd(t);
+#pragma unroll
+      for (int t = 0; t < NST; ++t) {
+        if (t + PF < NST) ring[t + PF] = rd(t + PF);
+        if (t == 2 * NS - 2) {
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            d4[a4] = *reinterpret_cast<const f32x4*>(dlt + 8 * a4 + 4 * hh);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const Op o = ring[t];
+        if (t < NS) {
+          sacc = mfma32x32x16(o.a, kRegK ? kreg[kRegK ? t : 0] : o.b, sacc);
+        } else if (t < 2 * NS) {
+          const int c = t - NS;
+          dpacc = mfma32x32x16(o.a, kRegV ? vreg[kRegV ? c : 0] : o.b, dpacc);
+          // P for this step's share of register pairs
+#pragma unroll
+          for (int pp = 8 * c / NS; pp < 8 * (c + 1) / NS; ++pp) {
+#pragma unroll
+            for (int e = 2 * pp; e < 2 * pp + 2; ++e) {
+              const float nl = ALIBI ? n4[e / 4][e % 4] + slj : n4[e / 4][e % 4];
+              float pr = fast_exp2(__builtin_fmaf(sacc[e], c2, nl));
+              if (kMasked) {
+                const int io = 8 * (e / 4) + e % 4;
+                if (io < lo_off || io > hi_off) pr = 0.0f;
+              }
+              sacc[e] = pr;
+            }
+            pw[pp / 4][pp % 4] = pack2(sacc[2 * pp], sacc[2 * pp + 1]);
           }
-          sacc[r] = pr;
-          dpacc[r] = pr * (dpacc[r] - d4[e]);
+        } else if (t < 2 * NS + NG) {
+          const int g = t - 2 * NS;
+          dvacc[g % NB] = mfma32x32x16(o.a, __builtin_bit_cast(elem8, pw[g / NB]), dvacc[g % NB]);
+          // dS' for this step's share of register pairs
+#pragma unroll
+          for (int pp = 8 * g / NG; pp < 8 * (g + 1) / NG; ++pp) {
+            float x[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * pp + e;
+              x[e] = sacc[r] * (dpacc[r] - d4[r / 4][r % 4]);
+            }
+            sw[pp / 4][pp % 4] = pack2(x[0], x[1]);
+          }
+        } else {
+          const int g = t - 2 * NS - NG;
+          dkacc[g % NB] = mfma32x32x16(o.a, __builtin_bit_cast(elem8, sw[g / NB]), dkacc[g % NB]);
         }
       }
-    };
-    if (!__all(lane_full)) {
-      asm volatile("" ::: "memory");  // keeps this a branch (no if-conversion)
-      pds(std::true_type{});
-    } else {
-      pds(std::false_type{});
-    }
-
-    elem8 pb[2], sb[2];
-#pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-      float pv[8], sv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = sacc[8 * qc + e];
-        sv[e] = dpacc[8 * qc + e];
-      }
-      pb[qc] = pack8(pv);
-      sb[qc] = pack8(sv);
-    }
-    // dO^T and Q~^T operands of (query chunk, dim block) g, read one MFMA
-    // pair ahead of their use.
-    constexpr int NG = 2 * NB;
-    auto tops = [&](int g) {
-      const int off = taddr[0][g % NB] + 16 * (g / NB) * D;
-      const int second = taddr[1][g % NB] - taddr[0][g % NB];
-      return Ops{tr8(Qt + off, second), tr8(Gt + off, second), elem8{}, elem8{}};
-    };
-    Ops tc = tops(0);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const Ops tn = g + 1 < NG ? tops(g + 1) : tc;
-      __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
-      dvacc[g % NB] = mfma32x32x16(tc.g, pb[g / NB], dvacc[g % NB]);
-      dkacc[g % NB] = mfma32x32x16(tc.q, sb[g / NB], dkacc[g % NB]);
-      tc = tn;
     }
   };
-  for (int qt = qt_lo; qt < qt_hi; ++qt) {
+  // A wave's q-tiles fall into three runs: masked ones before its first tile
+  // inside every row's range (the diagonal), unmasked ones, masked ones after
+  // (document ends).  One loop per run keeps one variant of the tile per loop.
+  auto full = [&](int qt) {
+    const int qw0 = qt * BMQ + 32 * qhalf;
+    return __all((qw0 >= qlo) && (qw0 + 31 <= qhi));
+  };
+  auto run = [&](auto masked, int qt) __attribute__((always_inline)) {
     const int buf = (qt - qt_lo) & 1;
-    tile(qt, lds + L::Q0 + buf * BMQ * D, lds + L::G0 + buf * BMQ * D,
+    tile(masked, qt, lds + L::Q0 + buf * BMQ * D, lds + L::G0 + buf * BMQ * D,
          lds + L::Q0 + (buf ^ 1) * BMQ * D, lds + L::KT, lds + L::VT, fl + buf * BMQ,
          fl + (buf ^ 1) * BMQ);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+  int qt = qt_lo;
+  for (; qt < qt_hi && !full(qt); ++qt) run(std::true_type{}, qt);
+  for (; qt < qt_hi && full(qt); ++qt) run(std::false_type{}, qt);
+  for (; qt < qt_hi; ++qt) run(std::true_type{}, qt);
 
-  // Epilogue: the two query halves of a key group add their dK~ / dV partial
-  // sums in fp32 over the (now idle) tile areas, then rows are written
-  // coalesced; dK = scale R^T dK~.
-  float* stage = reinterpret_cast<float*>(lds);
-  constexpr int FS = D + 4;
-  static_assert(BNK * FS * 4 <= L::F0 * 2, "epilogue staging must fit");
-  const int half = a.rd >> 1;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll 1
-    for (int hq = 1; hq >= 0; --hq) {
-      if (qhalf == hq) {
+  // Epilogue: the two query halves of a key group add their dK~ and dV partial
+  // sums in fp32 over the (now idle) LDS, then rows are written coalesced;
+  // dK = scale R^T dK~.
+  constexpr int FS = D + 4;          // staged row stride (floats)
+  constexpr int NIT = BNK * C / NT8;  // 8-dim row chunks per thread
+  static_assert(BNK * C % NT8 == 0, "row chunks must split evenly over the workgroup");
+  float* stk = reinterpret_cast<float*>(lds);
+  float* stv = stk + BNK * FS;
+  static_assert(2 * BNK * FS * 4 <= L::EPI_BYTES, "epilogue staging must fit");
+  auto epilogue = [&](auto rope_tag) __attribute__((always_inline)) {
+    constexpr bool kRope = decltype(rope_tag)::value;
+    const int rd = a.rd, half = rd >> 1;
+    // Query half 1 stores its sums, query half 0 adds its own (all reads
+    // issued before the first add) and stores the total.
+    if (qhalf == 1) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int off = (32 * kg + ql) * FS + 32 * db + 8 * a4 + 4 * hh;
+          f32x4 wk, wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wk[e] = dkacc[db][4 * a4 + e];
+            wv[e] = dvacc[db][4 * a4 + e];
+          }
+          *reinterpret_cast<f32x4*>(stk + off) = wk;
+          *reinterpret_cast<f32x4*>(stv + off) = wv;
+        }
+    }
+    __syncthreads();
+    if (qhalf == 0) {
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        float* st = pass == 0 ? stk : stv;
+        f32x4 o4[NB][4];
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            o4[db][a4] = *reinterpret_cast<const f32x4*>(st + (32 * kg + ql) * FS + 32 * db +
+                                                         8 * a4 + 4 * hh);
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
-            f32x4* dstp = reinterpret_cast<f32x4*>(stage + (32 * kg + ql) * FS + 32 * db + 8 * a4 +
-                                                   4 * hh);
             f32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              w[e] = pass == 0 ? dkacc[db][4 * a4 + e] * scale : dvacc[db][4 * a4 + e];
-            if (hq == 0) w += *dstp;
-            *dstp = w;
+              w[e] = pass == 0 ? (dkacc[db][4 * a4 + e] + o4[db][a4][e]) * scale
+                               : dvacc[db][4 * a4 + e] + o4[db][a4][e];
+            *reinterpret_cast<f32x4*>(st + (32 * kg + ql) * FS + 32 * db + 8 * a4 + 4 * hh) = w;
           }
-      }
-      __syncthreads();
-    }
-    void* outp = pass == 0 ? p.dk : p.dv;
-    const Strides so = pass == 0 ? p.sdk : p.sdv;
-    for (int it = tid; it < BNK * C; it += NT8) {
-      const int row = it / C, d0 = 8 * (it % C);
-      const int jj = k0 + row;
-      if (jj >= S) continue;
-      const float* srow_p = stage + row * FS;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        float y = srow_p[d];
-        if (pass == 0 && d < a.rd) {
-          const bool first = d < half;
-          const float2 cs = a.rope[(int64_t)jj * half + (first ? d : d - half)];
-          const float xp = srow_p[first ? d + half : d - half];
-          y = first ? (y * cs.x + xp * cs.y) : (y * cs.x - xp * cs.y);
-        }
-        x[e] = y;
-      }
-      if (p.out_f32) {
-        float* orow = (float*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
-        *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
-        *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
-      } else {
-        uint16_t* orow = (uint16_t*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
-        *reinterpret_cast<u32x4*>(orow) =
-            u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
       }
     }
     __syncthreads();
-  }
+    // The rotary table entries of this thread's dK rows are requested before
+    // the dV rows go out, so that their latency passes meanwhile.
+    float2 cs[NIT][8];
+    if constexpr (kRope) {
+#pragma unroll
+      for (int m = 0; m < NIT; ++m) {
+        const int it = tid + NT8 * m;
+        const int row = it / C, d0 = 8 * (it % C);
+        const float2* rrow = a.rope + (int64_t)min(k0 + row, S - 1) * half;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = min(d0 + e, rd - 1);
+          cs[m][e] = rrow[d < half ? d : d - half];
+        }
+      }
+    }
+
+    // Rows out: every staged value this thread needs is read first.
+#pragma unroll
+    for (int pass = 1; pass >= 0; --pass) {
+      void* outp = pass == 0 ? p.dk : p.dv;
+      const Strides so = pass == 0 ? p.sdk : p.sdv;
+      const float* st = pass == 0 ? stk : stv;
+      float x[NIT][8];
+#pragma unroll
+      for (int m = 0; m < NIT; ++m) {
+        const int it = tid + NT8 * m;
+        const int row = it / C, d0 = 8 * (it % C);
+        const float* srow_p = st + row * FS;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(srow_p + d0);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(srow_p + d0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[m][e] = lo[e];
+          x[m][4 + e] = hi[e];
+        }
+        if (kRope && pass == 0) {
+          // Rotary partners; dims past rd read themselves and keep their
+          // value (cos 1, sin 0), all without branches.
+          float xp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = d0 + e;
+            const int step = d < rd ? (d < half ? half : -half) : 0;
+            xp[e] = srow_p[d + step];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = d0 + e;
+            const bool r = d < rd;
+            const float cn = r ? cs[m][e].x : 1.0f;
+            const float sn = r ? (d < half ? cs[m][e].y : -cs[m][e].y) : 0.0f;
+            x[m][e] = x[m][e] * cn + xp[e] * sn;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NIT; ++m) {
+        const int it = tid + NT8 * m;
+        const int row = it / C, d0 = 8 * (it % C);
+        const int jj = k0 + row;
+        if (jj >= S) continue;
+        if (p.out_f32) {
+          float* orow = (float*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
+          *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
+          *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
+        } else {
+          uint16_t* orow = (uint16_t*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
+          *reinterpret_cast<u32x4*>(orow) =
+              u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
+                    pack2(x[m][6], x[m][7])};
+        }
+      }
+    }
+  };
+  if (a.rd > 0)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 // ------------------------------------------------------------------------ dQ
