@@ -617,10 +617,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int row = it / C, d0 = 8 * (it % C);
         const float2* rrow = a.rope + (int64_t)min(k0 + row, S - 1) * half;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = min(d0 + e, rd - 1);
-          cs[m][e] = rrow[d < half ? d : d - half];
-        }
+        for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
       }
     }
 
@@ -644,21 +641,13 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
           x[m][4 + e] = hi[e];
         }
         if (kRope && pass == 0) {
-          // Rotary partners; dims past rd read themselves and keep their
-          // value (cos 1, sin 0), all without branches.
           float xp[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = d0 + e;
-            const int step = d < rd ? (d < half ? half : -half) : 0;
-            xp[e] = srow_p[d + step];
-          }
+          for (int e = 0; e < 8; ++e) xp[e] = srow_p[d0 + e + rot_partner_step(d0 + e, half, rd)];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int d = d0 + e;
-            const bool r = d < rd;
-            const float cn = r ? cs[m][e].x : 1.0f;
-            const float sn = r ? (d < half ? cs[m][e].y : -cs[m][e].y) : 0.0f;
+            float cn, sn;
+            rot_t_factors(cs[m][e], d0 + e, half, rd, cn, sn);
             x[m][e] = x[m][e] * cn + xp[e] * sn;
           }
         }
@@ -915,48 +904,86 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 
   // Epilogue: stage this wave's 32 rows of dQ~ (fp32) in LDS, then write
   // dq = scale R^T dQ~ row-wise.  Register r of dim block db holds dim
-  // 32 db + 8 (r/4) + 4 hh + r%4 of query ql.
+  // 32 db + 8 (r/4) + 4 hh + r%4 of query ql.  The rotary table entries of the
+  // lane's rows are all requested at once (clamped indices, no branches), and
+  // every staged value a lane needs is read before any is used.
+  constexpr int NIT = 32 * C / 64;  // 8-dim row chunks per lane
+  static_assert(32 * C % 64 == 0, "row chunks must split evenly over the wave");
   float* stage = reinterpret_cast<float*>(lds) + wave * 32 * FS;
-#pragma unroll
-  for (int db = 0; db < NB; ++db)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      f32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = dqacc[db][4 * a4 + e];
-      *reinterpret_cast<f32x4*>(stage + ql * FS + 32 * db + 8 * a4 + 4 * hh) = w;
-    }
-  lds_wave_sync();
   const float scale = a.scale;
-  const int rd = a.rd, half = rd >> 1;
-  for (int it = lane; it < 32 * C; it += 64) {
-    const int row = it / C, d0 = 8 * (it % C);
-    const int i = q0 + 32 * wave + row;
-    if (i >= S) continue;
-    const float* srow = stage + row * FS;
-    float x[8];
+  auto epilogue = [&](auto rope_tag) __attribute__((always_inline)) {
+    constexpr bool kRope = decltype(rope_tag)::value;
+    const int rd = a.rd, half = rd >> 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d0 + e;
-      float y = srow[d];
-      if (d < rd) {
-        const bool first = d < half;
-        const float2 cs = a.rope[(int64_t)i * half + (first ? d : d - half)];
-        const float xp = srow[first ? d + half : d - half];
-        y = first ? (y * cs.x + xp * cs.y) : (y * cs.x - xp * cs.y);
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = dqacc[db][4 * a4 + e];
+        *reinterpret_cast<f32x4*>(stage + ql * FS + 32 * db + 8 * a4 + 4 * hh) = w;
       }
-      x[e] = y * scale;
+    lds_wave_sync();
+    float2 cs[NIT][8];
+    if constexpr (kRope) {
+#pragma unroll
+      for (int m = 0; m < NIT; ++m) {
+        const int it = lane + 64 * m;
+        const int row = it / C, d0 = 8 * (it % C);
+        const float2* rrow = a.rope + (int64_t)min(q0 + 32 * wave + row, S - 1) * half;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+      }
     }
-    if (p.out_f32) {
-      float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-      *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
-    } else {
-      uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-      *reinterpret_cast<u32x4*>(orow) =
-          u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+    float x[NIT][8];
+#pragma unroll
+    for (int m = 0; m < NIT; ++m) {
+      const int it = lane + 64 * m;
+      const int row = it / C, d0 = 8 * (it % C);
+      const float* srow = stage + row * FS;
+      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(srow + d0);
+      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(srow + d0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[m][e] = lo4[e];
+        x[m][4 + e] = hi4[e];
+      }
+      if constexpr (kRope) {
+        float xp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xp[e] = srow[d0 + e + rot_partner_step(d0 + e, half, rd)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float cn, sn;
+          rot_t_factors(cs[m][e], d0 + e, half, rd, cn, sn);
+          x[m][e] = x[m][e] * cn + xp[e] * sn;
+        }
+      }
     }
-  }
+#pragma unroll
+    for (int m = 0; m < NIT; ++m) {
+      const int it = lane + 64 * m;
+      const int row = it / C, d0 = 8 * (it % C);
+      const int i = q0 + 32 * wave + row;
+      if (i >= S) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[m][e] *= scale;
+      if (p.out_f32) {
+        float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+        *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
+        *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
+      } else {
+        uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+        *reinterpret_cast<u32x4*>(orow) =
+            u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
+                  pack2(x[m][6], x[m][7])};
+      }
+    }
+  };
+  if (a.rd > 0)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 template <int D>

@@ -139,6 +139,29 @@ __device__ __forceinline__ void rotate8_scalar(const uint16_t* row, int d0, floa
   }
 }
 
+// Transpose of the rotate-half rotation for dim d of a row, in integer and bit
+// operations only (no compares, so nothing is held in lane masks when a
+// caller unrolls many dims): the offset of d's rotary partner (+half below
+// half, -half below rd, 0 past rd) and the factors on x_d and on the partner
+// (cos and +-sin inside the rotary dims, 1 and 0 past them) given the table
+// entry cs of d (any finite value past rd).
+__device__ __forceinline__ int rot_partner_step(int d, int half, int rd) {
+  const int lt_half = (d - half) >> 31, lt_rd = (d - rd) >> 31;  // -1 when below
+  return ((half ^ ~lt_half) - ~lt_half) & lt_rd;
+}
+// Table column of dim d (d mod half, with d clamped below rd), also
+// compare-free.
+__device__ __forceinline__ int rot_table_col(int d, int half, int rd) {
+  const int dc = min(d, rd - 1);
+  return dc - (half & ~((dc - half) >> 31));
+}
+__device__ __forceinline__ void rot_t_factors(float2 cs, int d, int half, int rd, float& cn,
+                                              float& sn) {
+  const uint32_t lt_half = (uint32_t)((d - half) >> 31), lt_rd = (uint32_t)((d - rd) >> 31);
+  cn = __uint_as_float((__float_as_uint(cs.x) & lt_rd) | (0x3f800000u & ~lt_rd));
+  sn = __uint_as_float((__float_as_uint(cs.y) ^ (0x80000000u & ~lt_half)) & lt_rd);
+}
+
 // Workgroup order for kernels that stream one head's K/V (or Q/dO) tiles
 // from many workgroups (one per row tile).  Workgroups go to the 8 XCDs
 // round-robin (workgroup i on XCD i % 8), each XCD with its own 4 MB L2.
