@@ -131,8 +131,11 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     def avg(i, j):
         return sum(ev[i].elapsed_time(ev[j]) for ev in events) / len(events)
 
-    kernels_ms = {"fwd_rope_qk": avg(0, 1), "fwd": avg(1, 2), "bwd_pre": avg(3, 4),
-                  "bwd_dkdv": avg(4, 5), "bwd_dq": avg(5, 6)}
+    # backward events: start, after the rotation pass (none here: q~ and k~ are
+    # reused from the forward), after the dQ kernel (it also forms Delta and
+    # the lse term), after the dK/dV kernel
+    kernels_ms = {"fwd_rope_qk": avg(0, 1), "fwd": avg(1, 2), "bwd_dq": avg(4, 5),
+                  "bwd_dkdv": avg(5, 6)}
     return total_ms, kernels_ms
 
 
@@ -344,10 +347,6 @@ def main():
         "fwd_rope_qk": dict(bytes=2 * rows * wl.D * (el + 2)
                             if wl.rotary_dim > 0 and el == 2 else 0,
                             ms=kms["fwd_rope_qk"], bound="hbm"),
-        # preprocess: reads o, dO and lse, writes Delta and the row log-sum-exp term
-        # (the rotated q and k are reused from the forward's workspace)
-        "bwd_pre": dict(bytes=2 * rows * wl.D * el + rows * 12,
-                        ms=kms["bwd_pre"], bound="hbm"),
     }
     kern = {n: kd for n, kd in kern.items()
             if kd["ms"] > 0 and (kd["bound"] == "mfma" or kd["bytes"] > 0)}  # passes that ran

@@ -189,8 +189,8 @@ def neox_attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, *, pos: int = NEOX_POS_R
                      doc_offsets=None, out_f32: bool = False, workspace=None,
                      phase_events=None, reuse_rotated_qk: bool = False, stream=None) -> None:
     """Calls neox_attn_bwd_ex; strides are taken from the tensors.  ``phase_events``
-    is None or 4 events (before/after the preprocess, after the dK/dV kernel,
-    at the end).  ``reuse_rotated_qk``: the workspace was the
+    is None or 4 events (before/after the preprocess, after the dQ kernel --
+    the fp32 path: after its main kernels --, at the end).  ``reuse_rotated_qk``: the workspace was the
     forward's workspace and still holds the rotated q and k."""
     a, keep = _make_args(q, pos=pos, rotary_dim=rotary_dim, rope_base=rope_base,
                          alibi_slopes=alibi_slopes, causal=causal, softmax_scale=softmax_scale,

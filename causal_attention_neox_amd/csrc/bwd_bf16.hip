@@ -4,21 +4,23 @@
 // Recompute-based backward of the tiled exact attention (GPT-NeoX trains with
 // the FlashAttention-2 form, "GPT-NeoX 开源训练框架深度解读", section
 // "问题二：注意力计算太慢"): probabilities are rebuilt from the forward's row
-// logsumexp instead of being stored, so memory stays O(S).  Three passes:
+// logsumexp instead of being stored, so memory stays O(S).  Passes, in order:
 //
-//   prep:  per row, Delta_i = dO_i . o_i, nlse_i = -lse_i log2(e) (with the
-//          ALiBi row term folded in), and the rotated rows q~ = R q, k~ = R k
-//          written once to the workspace (NeoX rotate-half, "FasterTransformer
-//          GPT-NeoX 推理指南"), so the other passes never rotate; when the
-//          forward already left q~ and k~ in that workspace they are kept.
+//   prep:  the rotated rows q~ = R q, k~ = R k written once to the workspace
+//          (NeoX rotate-half, "FasterTransformer GPT-NeoX 推理指南"), so the
+//          other passes never rotate; skipped when the rotation is off or the
+//          forward already left q~ and k~ in that workspace.
+//   dQ:    one workgroup per (batch, head, 128 queries), Q-stationary.  Its
+//          prologue forms the row terms Delta_i = dO_i . o_i and
+//          nlse_i = -lse_i log2(e) (with the ALiBi row term folded in) and
+//          writes them to the workspace; 64-key tiles stream through LDS, S and
+//          dP are recomputed, dQ~ += dS' K~ accumulates in registers, and the
+//          epilogue writes dq = scale R^T dQ~.
 //   dK/dV: one workgroup per (batch, head, 128 keys), K-stationary; 64-row
-//          q-tiles stream through LDS:
+//          q-tiles (with their Delta and nlse) stream through LDS:
 //            S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
 //            dS' = P (dP - Delta),  dV^T += dO^T P,  dK~^T += Q~^T dS'.
 //          The epilogue writes dV and dK = scale R^T dK~.
-//   dQ:    one workgroup per (batch, head, 128 queries), Q-stationary; 64-key
-//          tiles stream through LDS, S and dP are recomputed, dQ~ += dS' K~
-//          accumulates in registers, and the epilogue writes dq = scale R^T dQ~.
 //
 // Splitting dQ off costs two extra products (S and dP recomputed) but needs
 // no fp32 atomics: accumulating dQ~ across key blocks with atomics is bound by
@@ -66,6 +68,9 @@ __device__ __forceinline__ int tpos(int row, int chunk) {
 
 // ------------------------------------------------------------------------ prep
 
+// q~ = R q and k~ = R k into the workspace, one row group of G lanes per row
+// (rotary partners exchanged through LDS).  Launched only when the rotation
+// is on and the forward did not leave q~ and k~ in the workspace.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   using RG = RowGroups<D>;
@@ -85,21 +90,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int d0 = 8 * g;
   const bool rot_lane = act && d0 < rd;
 
-  u32x4 ow = u32x4{0u, 0u, 0u, 0u}, gw = ow, qw = ow, kw = ow;
-  float lse = 0.0f;
+  u32x4 qw = u32x4{0u, 0u, 0u, 0u}, kw = qw;
   float2 cs[8];
   if (act) {
-    ow = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b + h * p.so.h +
-                                         (int64_t)i * p.so.s + d0);
-    gw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b + h * p.sdo.h +
-                                         (int64_t)i * p.sdo.s + d0);
-    if (rd > 0 && !p.qk_ready) {
-      qw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
-                                           (int64_t)i * p.sq.s + d0);
-      kw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
-                                           (int64_t)i * p.sk.s + d0);
-    }
-    if (g == 0) lse = p.lse[r];
+    qw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
+                                         (int64_t)i * p.sq.s + d0);
+    kw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
+                                         (int64_t)i * p.sk.s + d0);
   }
   if (rot_lane) {
 #pragma unroll
@@ -108,25 +105,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       cs[e] = d < rd ? a.rope[(int64_t)i * half + (d < half ? d : d - half)] : float2{1.0f, 0.0f};
     }
   }
-
-  float sum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sum = fmaf(el_lo(ow[e]), el_lo(gw[e]), sum);
-    sum = fmaf(el_hi(ow[e]), el_hi(gw[e]), sum);
-  }
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-  if (act) {
-    if (g == 0) {
-      p.delta[r] = sum;
-      float nl = -lse * kLog2e;
-      if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)i;
-      p.nlse[r] = nl;
-    }
-  }
-  if (rd == 0 || p.qk_ready) return;  // no rotation, or q~ and k~ already in place
-
   if (act) {
     *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][0][d0]) = qw;
     *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][1][d0]) = kw;
@@ -158,62 +136,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   if (act) {
     *reinterpret_cast<u32x4*>(p.qrot + (int64_t)r * D + d0) = qw;
     *reinterpret_cast<u32x4*>(p.krot + (int64_t)r * D + d0) = kw;
-  }
-}
-
-// Row terms only (no rotation to do: rotary off, or q~ and k~ already in the
-// workspace): Delta_i = dO_i . o_i and nlse_i.  Each wave takes NR row groups
-// and issues all their loads before the first use, so more bytes are in
-// flight per wave than in the rotating pass.
-constexpr int kDeltaRows = 4;  // row groups per wave
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  using RG = RowGroups<D>;
-  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW, NR = kDeltaRows;
-  const AttnShape& a = p.a;
-  const int S = a.S;
-  const int rows = a.B * a.H * S;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane & (G - 1), rw = lane / G;
-  const int wrow0 = (blockIdx.x * 4 + wave) * RPW * NR;
-  if (wrow0 >= rows) return;  // whole waves only
-  const int d0 = 8 * g;
-  u32x4 ow[NR], gw[NR];
-  float lse[NR];
-#pragma unroll
-  for (int n = 0; n < NR; ++n) {
-    const int r = wrow0 + n * RPW + rw;
-    ow[n] = gw[n] = u32x4{0u, 0u, 0u, 0u};
-    lse[n] = 0.0f;
-    if (r < rows && g < C) {
-      const int bh = r / S, i = r - bh * S;
-      const int b = bh / a.H, h = bh - b * a.H;
-      ow[n] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + b * p.so.b + h * p.so.h +
-                                              (int64_t)i * p.so.s + d0);
-      gw[n] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + b * p.sdo.b +
-                                              h * p.sdo.h + (int64_t)i * p.sdo.s + d0);
-      if (g == 0) lse[n] = p.lse[r];
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < NR; ++n) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sum = fmaf(el_lo(ow[n][e]), el_lo(gw[n][e]), sum);
-      sum = fmaf(el_hi(ow[n][e]), el_hi(gw[n][e]), sum);
-    }
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-    const int r = wrow0 + n * RPW + rw;
-    if (g == 0 && r < rows) {
-      const int bh = r / S, i = r - bh * S;
-      p.delta[r] = sum;
-      float nl = -lse[n] * kLog2e;
-      if (a.alibi) nl -= alibi_slope_log2(a, bh % a.H) * (float)i;
-      p.nlse[r] = nl;
-    }
   }
 }
 
@@ -782,18 +704,38 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
   fetch(kt_lo, lds, lds + 2 * TILE);
 
   // Q~ and dO of this lane's query as B operands: chunk c holds dims 16c + 8hh .. +7.
+  // The same chunks of o give Delta_i = dO_i . o_i (the lane halves add their
+  // partial sums); with lse_i it also forms nlse_i = -lse_i log2(e) (ALiBi:
+  // minus the row term).  Both go to the workspace for the dK/dV pass, which
+  // runs after this one.
   elem8 qreg[D / 16], greg[D / 16];
+  const uint16_t* ob = (const uint16_t*)p.o + b * p.so.b + h * p.so.h;
+  const float lse_i = p.lse[(int64_t)bh * S + qc];
+  float dsum = 0.0f;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     const int d0 = 16 * c + 8 * hh;
     u32x4 wq = *reinterpret_cast<const u32x4*>(qb + (int64_t)qc * qstr + d0);
     u32x4 wg = *reinterpret_cast<const u32x4*>(gb + (int64_t)qc * p.sdo.s + d0);
+    const u32x4 wo = *reinterpret_cast<const u32x4*>(ob + (int64_t)qc * p.so.s + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dsum = fmaf(el_lo(wo[e]), el_lo(wg[e]), dsum);
+      dsum = fmaf(el_hi(wo[e]), el_hi(wg[e]), dsum);
+    }
     if (qi >= S) wq = wg = u32x4{0u, 0u, 0u, 0u};
     qreg[c] = __builtin_bit_cast(elem8, wq);
     greg[c] = __builtin_bit_cast(elem8, wg);
   }
-  const float nl = qi < S ? p.nlse[(int64_t)bh * S + qi] : 0.0f;
-  const float dl = qi < S ? p.delta[(int64_t)bh * S + qi] : 0.0f;
+  dsum += __shfl_xor(dsum, 32);
+  float nl = -lse_i * kLog2e;
+  if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)qc;
+  if (qi < S && hh == 0) {
+    p.delta[(int64_t)bh * S + qi] = dsum;
+    p.nlse[(int64_t)bh * S + qi] = nl;
+  }
+  if (qi >= S) nl = 0.0f;
+  const float dl = qi < S ? dsum : 0.0f;
   const float c2 = a.scale_log2;
   const float sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
 
@@ -996,29 +938,25 @@ template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
   if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  if (p.a.rd == 0 || p.qk_ready) {
-    const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-    const int per_block = kDeltaRows * RowGroups<D>::RPB;
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + per_block - 1) / per_block)),
-                       dim3(256), 0, st, p);
-  } else {
+  if (p.a.rd > 0 && !p.qk_ready) {
     hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
+  // dQ first: it also writes Delta and nlse, which the dK/dV pass reads.
   const unsigned BH = (unsigned)(p.a.B * p.a.H);
-  const dim3 kgrid((unsigned)((p.a.S + BNK - 1) / BNK) * BH);
-  if (p.a.alibi)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(NT8), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(NT8), 0, st, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
   const dim3 qgrid((unsigned)((p.a.S + DQ_BM - 1) / DQ_BM) * BH);
   if (p.a.alibi)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
+  const dim3 kgrid((unsigned)((p.a.S + BNK - 1) / BNK) * BH);
+  if (p.a.alibi)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(NT8), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(NT8), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev, 3, st);
 }

@@ -111,8 +111,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t st, const hipEvent_t*
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
 
-// `ev` is null or 4 events recorded before the preprocess kernel, after it,
-// after the dK/dV kernel and at the end (after the dQ kernel or finalize).
+// `ev` is null or 4 events: before the first kernel, after the preprocess
+// kernel (if any), after the dQ kernel (16-bit paths: dQ runs first and also
+// writes Delta and nlse) or the fp32 main kernels, and at the end.
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);

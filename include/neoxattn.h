@@ -110,10 +110,13 @@ typedef struct neox_strides {
  *                on `stream` around its kernels, for timing by the caller: the
  *                forward records [0] before its first kernel, [1] after the q/k
  *                rotation pass (right after [0] when none runs) and [2] after
- *                the attention kernel; the backward records [0] before the
- *                preprocess kernel, [1] after it, [2] after the dK/dV kernel
- *                and [3] at its end (after the dQ kernel, or the fp32 path's
- *                dq finalize).  The events are owned by the caller.
+ *                the attention kernel; the backward records [0] before its
+ *                first kernel, [1] after the preprocess kernel (right after
+ *                [0] when none runs), [2] after the 16-bit paths' dQ kernel
+ *                (which also forms the row terms) or after the fp32 path's
+ *                two main kernels, and [3] at its end (after the dK/dV kernel,
+ *                or the fp32 path's dq finalize).  The events are owned by
+ *                the caller.
  *  reuse_rotated_qk  0 or 1, backward only (16-bit storage with rotary_dim > 0;
  *                ignored otherwise).  1 promises that the backward workspace
  *                already holds the rotated rows q~ and k~ because it was passed
