@@ -144,16 +144,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 // Eight waves, two per SIMD.  Wave w owns the 32 keys 32 (w & 3) .. +31 of
 // the workgroup's 128 and query half w >> 2 (32 rows) of every 64-row q-tile;
 // the two waves of a key group add their dV / dK~ partial sums in the
-// epilogue.  K~ and V are the B operands of S and dP: K~ held in registers up
-// to D = 96 and V at D = 64 (where they fit), else re-read from stationary LDS
-// tiles.
+// epilogue.  At D <= 96 a q-tile has 128 rows and each wave takes two 32-row
+// quarters of it (rows 32 qhalf and 32 qhalf + 64) between barriers, which
+// halves the barriers and tile loads per row.  K~ and V are the B operands of
+// S and dP: held in registers at D = 64 (where they fit), else re-read from
+// stationary LDS tiles.
 constexpr int kDkdvPrefetch = 1;  // MFMA steps between an LDS operand's read and its use
 
 template <int D>
 struct DkdvLds {
-  static constexpr int BMQ = 64;
+  // q-tile rows per barrier: 128 where the double-buffered tiles fit in LDS
+  // (each wave then takes two 32-row quarters of a tile), else 64.
+  static constexpr int BMQ = D <= 96 ? 128 : 64;
+  static constexpr int NQQ = BMQ / 64;  // quarters per wave per tile
   static constexpr int C = D / 8;
-  static constexpr bool kRegK = D <= 96;         // K~ B operands held in registers
+  static constexpr bool kRegK = D <= 64;         // K~ B operands held in registers
   static constexpr bool kRegV = D <= 64;         // V B operands held in registers
   static constexpr int KT = 0;                   // K~ [BNK][D] (staging for the registers)
   static constexpr int VT = KT + BNK * D;        // V [BNK][D] (when not in registers)
@@ -173,7 +178,10 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BMQ = L::BMQ;
   constexpr int C = L::C;
   constexpr int NB = D / 32;
-  constexpr int NFB = 2 * C / 8;  // 1 KB direct-load blocks per wave (per tile / stationary pair)
+  constexpr int NQQ = L::NQQ;
+  constexpr int CB = C * BMQ / 64;  // 1 KB blocks of one q-tile tensor (Q~ or dO)
+  constexpr int NFB = 2 * CB / 8;   // direct-load blocks per wave of a q-tile (Q~ and dO)
+  constexpr int NKB = 2 * C / 8;    // direct-load blocks per wave of the stationary K~ (or V)
   static_assert((2 * C) % 8 == 0, "tile blocks must split evenly over 8 waves");
   constexpr bool kRegK = L::kRegK, kRegV = L::kRegV;
   __shared__ __attribute__((aligned(16))) uint16_t lds[L::N16];
@@ -226,16 +234,16 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
   const int qt_lo = bqlo / BMQ, qt_hi = bqhi / BMQ + 1;
 
-  // Direct-load plan of a q-tile: 2C blocks of 64 chunks (C of Q~, then C of
-  // dO); this wave loads blocks wave + 8 n.  Position P = 64 * blk + lane of a
-  // tile -> (row P / C, chunk (P % C) ^ swizzle(row)).
+  // Direct-load plan of a q-tile: 2 CB blocks of 64 chunks (CB of Q~, then
+  // CB of dO); this wave loads blocks wave + 8 n.  Position P = 64 * blk +
+  // lane of a tile -> (row P / C, chunk (P % C) ^ swizzle(row)).
   int foff[NFB], fdst[NFB];
   bool fdo[NFB];
 #pragma unroll
   for (int n = 0; n < NFB; ++n) {
     const int fbk = wave + 8 * n;
-    fdo[n] = fbk >= C;
-    const int blk = fdo[n] ? fbk - C : fbk;
+    fdo[n] = fbk >= CB;
+    const int blk = fdo[n] ? fbk - CB : fbk;
     const int P = 64 * blk + lane;
     const int row = P / C, ch = (P % C) ^ swz<C>(row);
     foff[n] = (int)(row * (fdo[n] ? p.sdo.s : qstr)) + 8 * ch;
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int n = 0; n < NFB; ++n) {
         const int fbk = wave + 8 * n;
-        const int blk = fdo[n] ? fbk - C : fbk;
+        const int blk = fdo[n] ? fbk - CB : fbk;
         const int P = 64 * blk + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
         const int rr = min(q0 + row, S - 1);
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   // Stationary K~ (and V) tiles (2C blocks each, rows past S repeat row S-1)
   // and the first q-tile.
 #pragma unroll
-  for (int n = 0; n < NFB; ++n) {
+  for (int n = 0; n < NKB; ++n) {
     const int blk = wave + 8 * n;
     const int P = 64 * blk + lane;
     const int row = P / C, ch = (P % C) ^ swz<C>(row);
@@ -307,10 +315,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int c = 0; c < D / 16; ++c)
       kreg[c] = lds_read8(lds + L::KT + 8 * tpos<C>(32 * kg + ql, 2 * c + hh));
   }
-  const int kq_delta = 32 * C * 8 * (kg - qhalf);  // K~ row 32 kg + ql vs Q~ row 32 qhalf + ql
-
   // Operand offsets (elements).  Row reads of Q~ / dO (A of S and dP): row
-  // 32 qhalf + ql, chunk 2c + hh.  Transposed reads of a [rows][C chunks]
+  // 32 qhalf + ql (+ 64 in the second quarter), chunk 2c + hh.  Transposed reads of a [rows][C chunks]
   // tile: lane 16g + j16 supplies row 16 t + 4 hh + j16/4 (+8 for the second
   // read), 4 columns at chunk 4 db + 2 (g&1) + (j16&3)/2, half (j16&1).
   const int rsw = swz<C>(ql);
@@ -324,6 +330,15 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int db = 0; db < NB; ++db)
       taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) +
                       thalf + 32 * qhalf * D;
+  // Row-read offsets: Q~ / dO row 32 qhalf + ql (the second quarter adds the
+  // constant 64 rows), K~ / V row 32 kg + ql.
+  constexpr int NS = D / 16;  // dims steps of S and dP
+  int rofs[NS], kofs[NS];
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    rofs[c] = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
+    kofs[c] = 8 * ((32 * kg + ql) * C + ((2 * c + hh) ^ rsw));
+  }
 
   const float c2 = a.scale_log2;
   const float scale = a.scale;
@@ -344,23 +359,24 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
                   const uint16_t* __restrict__ VTp, const float* __restrict__ Fc,
                   float* __restrict__ Fn) __attribute__((always_inline)) {
     const int q0 = qt * BMQ;
-    const float* nlt = Fc + 32 * qhalf;
-    const float* dlt = Fc + 2 * BMQ + 32 * qhalf;
     if (qt + 1 < qt_hi) fetch_q(qt + 1, Qn, Fn);
-
-    const int qw0 = q0 + 32 * qhalf;
+  // Quarter r of this wave (r = 0, 1): its rows 32 qhalf + 64 r .. + 31.
+  auto quarter = [&](auto rc) __attribute__((always_inline)) {
+    constexpr int R = decltype(rc)::value;
+    constexpr int RQ = 8 * 64 * R * C;  // element offset of the quarter's rows
+    const float* nlt = Fc + 32 * qhalf + 64 * R;
+    const float* dlt = Fc + 2 * BMQ + 32 * qhalf + 64 * R;
+    const int qw0 = q0 + 32 * qhalf + 64 * R;
 
     // The tile in four product groups, each MFMA independent of the VALU work
     // placed beside it so that the two overlap:
     //   S = Q~ K~^T;  dP = dO V^T beside P = exp2(S scale log2e + nlse);
     //   dV^T += dO^T P beside dS' = P (dP - Delta);  dK~^T += Q~^T dS'.
     // (The softmax scale is applied to dK~ at the end.)  Register r of S / dP
-    // is query q0 + 32 qhalf + 8 (r/4) + 4 hh + r%4.
+    // is query qw0 + 8 (r/4) + 4 hh + r%4.
     {
       constexpr bool kMasked = decltype(masked)::value;
-      constexpr int NS = D / 16;  // dims steps of S and dP
       const int lo_off = qlo - qw0 - 4 * hh, hi_off = qhi - qw0 - 4 * hh;
-      auto roff = [&](int c) { return 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw)); };
       // nlse of this lane's rows now; Delta is read during the last dP step.
       f32x4 n4[4], d4[4];
 #pragma unroll
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       // reads.
       constexpr int NG = 2 * NB;
       auto top = [&](const uint16_t* T, int g) {
-        const int off = taddr[0][g % NB] + 16 * (g / NB) * D;
+        const int off = taddr[0][g % NB] + 16 * (g / NB) * D + 64 * R * D;
         return tr8(T + off, taddr[1][g % NB] - taddr[0][g % NB]);
       };
       // One stream of MFMA steps: S (NS), dP (NS), dV (NG), dK (NG); each
@@ -383,11 +399,11 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       auto rd = [&](int t) {
         Op o;
         if (t < NS) {
-          o.a = lds_read8(Qt + roff(t));
-          o.b = kRegK ? o.a : lds_read8(KTp + roff(t) + kq_delta);
+          o.a = lds_read8(Qt + rofs[t] + RQ);
+          o.b = kRegK ? o.a : lds_read8(KTp + kofs[t]);
         } else if (t < 2 * NS) {
-          o.a = lds_read8(Gt + roff(t - NS));
-          o.b = kRegV ? o.a : lds_read8(VTp + roff(t - NS) + kq_delta);
+          o.a = lds_read8(Gt + rofs[t - NS] + RQ);
+          o.b = kRegV ? o.a : lds_read8(VTp + kofs[t - NS]);
         } else if (t < 2 * NS + NG) {
           o.a = top(Gt, t - 2 * NS);
           o.b = o.a;
@@ -453,12 +469,15 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
   };
+    quarter(std::integral_constant<int, 0>{});
+    if constexpr (NQQ == 2) quarter(std::integral_constant<int, 1>{});
+  };
   // A wave's q-tiles fall into three runs: masked ones before its first tile
   // inside every row's range (the diagonal), unmasked ones, masked ones after
   // (document ends).  One loop per run keeps one variant of the tile per loop.
   auto full = [&](int qt) {
-    const int qw0 = qt * BMQ + 32 * qhalf;
-    return __all((qw0 >= qlo) && (qw0 + 31 <= qhi));
+    const int qw0 = qt * BMQ + 32 * qhalf;  // first row of the wave's first quarter
+    return __all((qw0 >= qlo) && (qw0 + 64 * (NQQ - 1) + 31 <= qhi));
   };
   auto run = [&](auto masked, int qt) __attribute__((always_inline)) {
     const int buf = (qt - qt_lo) & 1;
