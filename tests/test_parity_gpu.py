@@ -43,6 +43,9 @@ SMALL = [
     (2, 2, 300, 128, 128, "bf16", True, False),
     (1, 2, 257, 128, 40, "bf16", True, False),
     (1, 2, 200, 64, 6, "bf16", True, False),
+    (1, 2, 333, 96, 24, "bf16", True, False),   # several 128-row dK/dV q-tiles, ragged tail
+    (1, 2, 517, 96, 96, "bf16", True, False),
+    (1, 2, 390, 64, 16, "bf16", True, False),
     (1, 2, 190, 128, 128, "bf16", False, False),
     (1, 4, 300, 128, 0, "bf16", True, True),
     (1, 2, 150, 96, 0, "bf16", False, True),
