@@ -496,8 +496,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   // sums in fp32 over the (now idle) LDS, then rows are written coalesced;
   // dK = scale R^T dK~.
   constexpr int FS = D + 4;          // staged row stride (floats)
-  constexpr int NIT = BNK * C / NT8;  // 8-dim row chunks per thread
-  static_assert(BNK * C % NT8 == 0, "row chunks must split evenly over the workgroup");
+  constexpr int NIT = C / 4;  // 8-dim row chunks per thread (128 rows, 4 chunk groups)
+  static_assert(C % 4 == 0 && NT8 == 4 * BNK, "row chunks must split evenly over the workgroup");
   float* stk = reinterpret_cast<float*>(lds);
   float* stv = stk + BNK * FS;
   static_assert(2 * BNK * FS * 4 <= L::EPI_BYTES, "epilogue staging must fit");
@@ -548,32 +548,38 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    // The rotary table entries of this thread's dK rows are requested before
-    // the dV rows go out, so that their latency passes meanwhile.
+    // Rows out, chunk m of this thread: with the rotation on part of the dims
+    // (0 < rd < D, D <= 96) thread t takes row t % 128, chunk 4 m + t / 128, so a chunk
+    // pass touches the rotary dims (or not) for a whole wave and the rotary
+    // work is skipped where it is not; otherwise consecutive threads take
+    // consecutive chunks of a row (whole rows per store instruction).  The
+    // rotary table entries of the thread's dK chunks are requested before the
+    // dV rows go out, so that their latency passes meanwhile; every staged
+    // value is read before any is used.
+    const bool part = kRope && D <= 96 && rd < D;  // (at D = 128 the row-major order measured faster)
+    auto crow = [&](int m) { return part ? (tid & (BNK - 1)) : (tid + NT8 * m) / C; };
+    auto cd0 = [&](int m) { return part ? 8 * (4 * m + tid / BNK) : 8 * ((tid + NT8 * m) % C); };
     float2 cs[NIT][8];
     if constexpr (kRope) {
 #pragma unroll
       for (int m = 0; m < NIT; ++m) {
-        const int it = tid + NT8 * m;
-        const int row = it / C, d0 = 8 * (it % C);
-        const float2* rrow = a.rope + (int64_t)min(k0 + row, S - 1) * half;
+        const int d0 = cd0(m);
+        if (!part || d0 < rd) {
+          const float2* rrow = a.rope + (int64_t)min(k0 + crow(m), S - 1) * half;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+          for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+        }
       }
     }
-
-    // Rows out: every staged value this thread needs is read first.
 #pragma unroll
     for (int pass = 1; pass >= 0; --pass) {
       void* outp = pass == 0 ? p.dk : p.dv;
       const Strides so = pass == 0 ? p.sdk : p.sdv;
-      const float* st = pass == 0 ? stk : stv;
       float x[NIT][8];
 #pragma unroll
       for (int m = 0; m < NIT; ++m) {
-        const int it = tid + NT8 * m;
-        const int row = it / C, d0 = 8 * (it % C);
-        const float* srow_p = st + row * FS;
+        const int d0 = cd0(m);
+        const float* srow_p = (pass == 0 ? stk : stv) + crow(m) * FS;
         const f32x4 lo = *reinterpret_cast<const f32x4*>(srow_p + d0);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(srow_p + d0 + 4);
 #pragma unroll
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
           x[m][e] = lo[e];
           x[m][4 + e] = hi[e];
         }
-        if (kRope && pass == 0) {
+        if (kRope && pass == 0 && (!part || d0 < rd)) {
           float xp[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) xp[e] = srow_p[d0 + e + rot_partner_step(d0 + e, half, rd)];
@@ -595,19 +601,18 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int m = 0; m < NIT; ++m) {
-        const int it = tid + NT8 * m;
-        const int row = it / C, d0 = 8 * (it % C);
-        const int jj = k0 + row;
-        if (jj >= S) continue;
-        if (p.out_f32) {
-          float* orow = (float*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
-          *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
-          *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
-        } else {
-          uint16_t* orow = (uint16_t*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
-          *reinterpret_cast<u32x4*>(orow) =
-              u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
-                    pack2(x[m][6], x[m][7])};
+        const int d0 = cd0(m), jj = k0 + crow(m);
+        if (jj < S) {
+          if (p.out_f32) {
+            float* orow = (float*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
+            *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
+            *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
+          } else {
+            uint16_t* orow = (uint16_t*)outp + b * so.b + h * so.h + (int64_t)jj * so.s + d0;
+            *reinterpret_cast<u32x4*>(orow) =
+                u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
+                      pack2(x[m][6], x[m][7])};
+          }
         }
       }
     }
@@ -865,11 +870,13 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 
   // Epilogue: stage this wave's 32 rows of dQ~ (fp32) in LDS, then write
   // dq = scale R^T dQ~ row-wise.  Register r of dim block db holds dim
-  // 32 db + 8 (r/4) + 4 hh + r%4 of query ql.  The rotary table entries of the
-  // lane's rows are all requested at once (clamped indices, no branches), and
-  // every staged value a lane needs is read before any is used.
-  constexpr int NIT = 32 * C / 64;  // 8-dim row chunks per lane
-  static_assert(32 * C % 64 == 0, "row chunks must split evenly over the wave");
+  // 32 db + 8 (r/4) + 4 hh + r%4 of query ql.  Lane (ql, hh) writes chunks
+  // 2m + hh of row ql, so a pass m either touches the rotary dims (16 m < rd)
+  // or not, for the whole wave: the rotary table entries are requested, all at
+  // once, only for the passes that need them, and every staged value a lane
+  // needs is read before any is used.
+  constexpr int NIT = C / 2;  // passes: chunks 2m and 2m + 1 of the 32 rows
+  static_assert(C % 2 == 0, "row chunks must pair up");
   float* stage = reinterpret_cast<float*>(lds) + wave * 32 * FS;
   const float scale = a.scale;
   auto epilogue = [&](auto rope_tag) __attribute__((always_inline)) {
@@ -885,23 +892,24 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
         *reinterpret_cast<f32x4*>(stage + ql * FS + 32 * db + 8 * a4 + 4 * hh) = w;
       }
     lds_wave_sync();
+    const int i = q0 + 32 * wave + ql;  // this lane's row
+    const float* srow = stage + ql * FS;
     float2 cs[NIT][8];
     if constexpr (kRope) {
+      const float2* rrow = a.rope + (int64_t)min(i, S - 1) * half;
 #pragma unroll
       for (int m = 0; m < NIT; ++m) {
-        const int it = lane + 64 * m;
-        const int row = it / C, d0 = 8 * (it % C);
-        const float2* rrow = a.rope + (int64_t)min(q0 + 32 * wave + row, S - 1) * half;
+        if (16 * m < rd) {
+          const int d0 = 8 * (2 * m + hh);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+          for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+        }
       }
     }
     float x[NIT][8];
 #pragma unroll
     for (int m = 0; m < NIT; ++m) {
-      const int it = lane + 64 * m;
-      const int row = it / C, d0 = 8 * (it % C);
-      const float* srow = stage + row * FS;
+      const int d0 = 8 * (2 * m + hh);
       const f32x4 lo4 = *reinterpret_cast<const f32x4*>(srow + d0);
       const f32x4 hi4 = *reinterpret_cast<const f32x4*>(srow + d0 + 4);
 #pragma unroll
@@ -909,7 +917,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
         x[m][e] = lo4[e];
         x[m][4 + e] = hi4[e];
       }
-      if constexpr (kRope) {
+      if (kRope && 16 * m < rd) {
         float xp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) xp[e] = srow[d0 + e + rot_partner_step(d0 + e, half, rd)];
@@ -921,23 +929,22 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
+    if (i < S) {
 #pragma unroll
-    for (int m = 0; m < NIT; ++m) {
-      const int it = lane + 64 * m;
-      const int row = it / C, d0 = 8 * (it % C);
-      const int i = q0 + 32 * wave + row;
-      if (i >= S) continue;
+      for (int m = 0; m < NIT; ++m) {
+        const int d0 = 8 * (2 * m + hh);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[m][e] *= scale;
-      if (p.out_f32) {
-        float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-        *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
-        *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
-      } else {
-        uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
-        *reinterpret_cast<u32x4*>(orow) =
-            u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
-                  pack2(x[m][6], x[m][7])};
+        for (int e = 0; e < 8; ++e) x[m][e] *= scale;
+        if (p.out_f32) {
+          float* orow = (float*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+          *reinterpret_cast<f32x4*>(orow) = f32x4{x[m][0], x[m][1], x[m][2], x[m][3]};
+          *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[m][4], x[m][5], x[m][6], x[m][7]};
+        } else {
+          uint16_t* orow = (uint16_t*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+          *reinterpret_cast<u32x4*>(orow) =
+              u32x4{pack2(x[m][0], x[m][1]), pack2(x[m][2], x[m][3]), pack2(x[m][4], x[m][5]),
+                    pack2(x[m][6], x[m][7])};
+        }
       }
     }
   };
