@@ -565,9 +565,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       for (int m = 0; m < NIT; ++m) {
         const int d0 = cd0(m);
         if (!part || d0 < rd) {
-          const float2* rrow = a.rope + (int64_t)min(k0 + crow(m), S - 1) * half;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
+          rope_entries8(a.rope + (int64_t)min(k0 + crow(m), S - 1) * half, d0, half, rd, cs[m]);
         }
       }
     }
@@ -899,11 +897,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
       const float2* rrow = a.rope + (int64_t)min(i, S - 1) * half;
 #pragma unroll
       for (int m = 0; m < NIT; ++m) {
-        if (16 * m < rd) {
-          const int d0 = 8 * (2 * m + hh);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cs[m][e] = rrow[rot_table_col(d0 + e, half, rd)];
-        }
+        if (16 * m < rd) rope_entries8(rrow, 8 * (2 * m + hh), half, rd, cs[m]);
       }
     }
     float x[NIT][8];

@@ -149,11 +149,30 @@ __device__ __forceinline__ int rot_partner_step(int d, int half, int rd) {
   const int lt_half = (d - half) >> 31, lt_rd = (d - rd) >> 31;  // -1 when below
   return ((half ^ ~lt_half) - ~lt_half) & lt_rd;
 }
-// Table column of dim d (d mod half, with d clamped below rd), also
-// compare-free.
-__device__ __forceinline__ int rot_table_col(int d, int half, int rd) {
-  const int dc = min(d, rd - 1);
-  return dc - (half & ~((dc - half) >> 31));
+// The (cos, sin) table entries of dims d0 .. d0 + 7 (d0 a multiple of 8) from
+// the table row `rrow` (half entries): column d mod half for d < rd; dims past
+// rd get some valid entry (callers use cos 1, sin 0 there).  With half even a
+// pair of dims (d, d + 1), d even, never straddles half and its two entries
+// are 16-byte aligned, so four loads suffice; else eight.
+__device__ __forceinline__ void rope_entries8(const float2* rrow, int d0, int half, int rd,
+                                              float2* cs) {
+  if ((half & 1) == 0) {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int d = d0 + 2 * e2;
+      const int lt_half = (d - half) >> 31, lt_rd = (d - rd) >> 31;  // -1 when below
+      const int col = (d - (half & ~lt_half)) & lt_rd;                // 0 past rd
+      const f32x4 v = *reinterpret_cast<const f32x4*>(rrow + col);
+      cs[2 * e2] = float2{v[0], v[1]};
+      cs[2 * e2 + 1] = float2{v[2], v[3]};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dc = min(d0 + e, rd - 1);
+      cs[e] = rrow[dc - (half & ~((dc - half) >> 31))];
+    }
+  }
 }
 __device__ __forceinline__ void rot_t_factors(float2 cs, int d, int half, int rd, float& cn,
                                               float& sn) {

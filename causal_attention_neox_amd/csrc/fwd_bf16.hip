@@ -589,16 +589,8 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
     }
   }
 #pragma unroll
-  for (int n = 0; n < NR; ++n) {
-    if (act[n] && d0 < rd) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        cs[n][e] = d < rd ? a.rope[(int64_t)pos[n] * half + (d < half ? d : d - half)]
-                          : float2{1.0f, 0.0f};
-      }
-    }
-  }
+  for (int n = 0; n < NR; ++n)
+    if (act[n] && d0 < rd) rope_entries8(a.rope + (int64_t)pos[n] * half, d0, half, rd, cs[n]);
 #pragma unroll
   for (int n = 0; n < NR; ++n)
     if (act[n]) {
