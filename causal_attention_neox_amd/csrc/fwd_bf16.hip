@@ -554,8 +554,9 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
 }
 
 // q~ = R q and k~ = R k for every row, into contiguous bf16 [B][H][S][D]
-// buffers (one pass: both use the row's own position).  Each wave handles NR
-// row groups with every load issued before the first use.
+// buffers (one pass: both use the row's own position).  A wave handles NR
+// row groups of one position in RPW * NR heads, so the rotary table entries
+// are loaded once for all its rows; every load is issued before the first use.
 template <int D>
 __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
   using RG = RowGroups<D>;
@@ -563,23 +564,24 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][NR][RPW][2][D];
   const AttnShape& a = p.a;
   const int S = a.S, rd = a.rd, half = rd >> 1;
-  const int rows = a.B * a.H * S;
+  const int BH = a.B * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane & (G - 1), rw = lane / G;
-  const int wrow0 = (blockIdx.x * 4 + wave) * RPW * NR;
-  if (wrow0 >= rows) return;  // whole waves only
+  const int wid = blockIdx.x * 4 + wave;
+  const int i = wid % S, bh0 = (wid / S) * (RPW * NR);  // position; first head of the wave
+  if (bh0 >= BH) return;  // whole waves only
   const int d0 = 8 * g;
-  int r[NR], pos[NR];
+  int r[NR];
   bool act[NR];
   u32x4 w[NR][2];
-  float2 cs[NR][8];
+  float2 cs[8];
+  if (g < C && d0 < rd) rope_entries8(a.rope + (int64_t)i * half, d0, half, rd, cs);
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
-    r[n] = wrow0 + n * RPW + rw;
-    act[n] = r[n] < rows && g < C;
-    const int bh = r[n] / S, i = r[n] - bh * S;
+    const int bh = bh0 + n * RPW + rw;
+    r[n] = bh * S + i;
+    act[n] = bh < BH && g < C;
     const int b = bh / a.H, h = bh - b * a.H;
-    pos[n] = i;
     w[n][0] = w[n][1] = u32x4{0u, 0u, 0u, 0u};
     if (act[n]) {
       w[n][0] = *reinterpret_cast<const u32x4*>((const uint16_t*)p.q + b * p.sq.b + h * p.sq.h +
@@ -588,9 +590,6 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
                                                 (int64_t)i * p.sk.s + d0);
     }
   }
-#pragma unroll
-  for (int n = 0; n < NR; ++n)
-    if (act[n] && d0 < rd) rope_entries8(a.rope + (int64_t)pos[n] * half, d0, half, rd, cs[n]);
 #pragma unroll
   for (int n = 0; n < NR; ++n)
     if (act[n]) {
@@ -615,9 +614,9 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
           const int d = d0 + e;
           if (d < rd) {
             const bool first = d < half;
-            const float sn = first ? -cs[n][e].y : cs[n][e].y;  // rotate-half: (-x2, x1)
+            const float sn = first ? -cs[e].y : cs[e].y;  // rotate-half: (-x2, x1)
             x[e] = fmaf(el2f(rowbuf[wave][n][rw][t][first ? d + half : d - half]), sn,
-                        x[e] * cs[n][e].x);
+                        x[e] * cs[e].x);
           }
         }
         w[n][t] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
@@ -645,9 +644,10 @@ hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) 
     return launch_d<D, 0, true, false>(p, st);
   }
   if (rd > 0 && p.qrot) {
-    const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-    const int rows_per_block = 2 * RowGroups<D>::RPB;
-    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+    // one wave per (position, group of 2 RPW heads), four waves per block
+    const int64_t hpw = 2 * RowGroups<D>::RPW;
+    const int64_t waves = (p.a.B * p.a.H + hpw - 1) / hpw * p.a.S;
+    const dim3 grid((unsigned)((waves + 3) / 4));
     hipLaunchKernelGGL((rope_qk_kernel<D>), grid, dim3(256), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
