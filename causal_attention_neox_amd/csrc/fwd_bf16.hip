@@ -557,10 +557,12 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
 // buffers (one pass: both use the row's own position).  A wave handles NR
 // row groups of one position in RPW * NR heads, so the rotary table entries
 // are loaded once for all its rows; every load is issued before the first use.
+constexpr int kRopeNR = 2;  // row groups (of RPW heads) per wave in the rotation pass
+
 template <int D>
 __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
   using RG = RowGroups<D>;
-  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW, NR = 2;
+  constexpr int C = RG::C, G = RG::G, RPW = RG::RPW, NR = kRopeNR;
   __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][NR][RPW][2][D];
   const AttnShape& a = p.a;
   const int S = a.S, rd = a.rd, half = rd >> 1;
@@ -644,8 +646,8 @@ hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) 
     return launch_d<D, 0, true, false>(p, st);
   }
   if (rd > 0 && p.qrot) {
-    // one wave per (position, group of 2 RPW heads), four waves per block
-    const int64_t hpw = 2 * RowGroups<D>::RPW;
+    // one wave per (position, group of kRopeNR * RPW heads), four waves per block
+    const int64_t hpw = kRopeNR * RowGroups<D>::RPW;
     const int64_t waves = (p.a.B * p.a.H + hpw - 1) / hpw * p.a.S;
     const dim3 grid((unsigned)((waves + 3) / 4));
     hipLaunchKernelGGL((rope_qk_kernel<D>), grid, dim3(256), 0, st, p);
