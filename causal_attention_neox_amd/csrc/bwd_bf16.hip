@@ -69,8 +69,10 @@ __device__ __forceinline__ int tpos(int row, int chunk) {
 // ------------------------------------------------------------------------ prep
 
 // q~ = R q and k~ = R k into the workspace, one row group of G lanes per row
-// (rotary partners exchanged through LDS).  Launched only when the rotation
-// is on and the forward did not leave q~ and k~ in the workspace.
+// (rotary partners exchanged through LDS); a wave takes one position in RPW
+// heads, so the rotary table entries are loaded once for its rows.  Launched
+// only when the rotation is on and the forward did not leave q~ and k~ in
+// the workspace.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   using RG = RowGroups<D>;
@@ -78,14 +80,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t rowbuf[4][RPW][2][D];
   const AttnShape& a = p.a;
   const int S = a.S, rd = a.rd, half = rd >> 1;
-  const int rows = a.B * a.H * S;
+  const int BH = a.B * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane & (G - 1), rw = lane / G;
-  const int wrow0 = (blockIdx.x * 4 + wave) * RPW;
-  if (wrow0 >= rows) return;  // whole waves only
-  const int r = wrow0 + rw;
-  const bool act = r < rows && g < C;
-  const int bh = r / S, i = r - bh * S;
+  const int wid = blockIdx.x * 4 + wave;
+  const int i = wid % S, bh0 = (wid / S) * RPW;  // position; first head of the wave
+  if (bh0 >= BH) return;                          // whole waves only
+  const int bh = bh0 + rw;
+  const int r = bh * S + i;
+  const bool act = bh < BH && g < C;
   const int b = bh / a.H, h = bh - b * a.H;
   const int d0 = 8 * g;
   const bool rot_lane = act && d0 < rd;
@@ -98,13 +101,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     kw = *reinterpret_cast<const u32x4*>((const uint16_t*)p.k + b * p.sk.b + h * p.sk.h +
                                          (int64_t)i * p.sk.s + d0);
   }
-  if (rot_lane) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = d0 + e;
-      cs[e] = d < rd ? a.rope[(int64_t)i * half + (d < half ? d : d - half)] : float2{1.0f, 0.0f};
-    }
-  }
+  if (g < C && d0 < rd) rope_entries8(a.rope + (int64_t)i * half, d0, half, rd, cs);
   if (act) {
     *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][0][d0]) = qw;
     *reinterpret_cast<u32x4*>(&rowbuf[wave][rw][1][d0]) = kw;
@@ -948,10 +945,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     epilogue(std::false_type{});
 }
 
+// One wave per (position, group of RPW heads), four waves per block.
 template <int D>
 dim3 row_grid(const BwdParams& p) {
-  const int64_t rows = (int64_t)p.a.B * p.a.H * p.a.S;
-  return dim3((unsigned)((rows + RowGroups<D>::RPB - 1) / RowGroups<D>::RPB));
+  const int64_t hpw = RowGroups<D>::RPW;
+  const int64_t waves = (p.a.B * p.a.H + hpw - 1) / hpw * p.a.S;
+  return dim3((unsigned)((waves + 3) / 4));
 }
 
 template <int D>
