@@ -46,6 +46,8 @@ SMALL = [
     (1, 2, 333, 96, 24, "bf16", True, False),   # several 128-row dK/dV q-tiles, ragged tail
     (1, 2, 517, 96, 96, "bf16", True, False),
     (1, 2, 390, 64, 16, "bf16", True, False),
+    (3, 5, 70, 96, 24, "bf16", True, False),    # rotation passes: several head groups, the last partial
+    (2, 9, 45, 64, 16, "bf16", True, False),
     (1, 2, 190, 128, 128, "bf16", False, False),
     (1, 4, 300, 128, 0, "bf16", True, True),
     (1, 2, 150, 96, 0, "bf16", False, True),
