@@ -283,3 +283,16 @@ def test_fp8_forward_validation(lib, kw, status):
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present on this host")
 def test_valid_fp8_forward_without_gpu_fails_loudly(lib):
     assert fp8(lib) == E_DEV
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more ends with a message and
+    a non-zero status before any GPU work."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
