@@ -474,7 +474,22 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
   st.tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + 2 * TILE, wave);
 
   // Q~ of this lane's row as the B operand: chunk c holds dims 16c + 8hh .. +7.
-  {
+  // Rotation-free: the wave's 32 rows are loaded whole (16 bytes per lane, D / 8
+  // lanes per row, rows past S clamped) straight into a free part of the
+  // second tile buffer, chunk c of row r at position c ^ (r & QSW) (row-wise
+  // writes and column-wise reads both conflict-free), and read back in the
+  // operand layout after the prologue barrier.
+  constexpr int QSW = CPR == 16 ? 15 : (CPR == 8 ? 7 : 3);
+  uint16_t* qrows = lds + ((wave & 2) ? 3 * TILE : TILE) + (wave & 1) * 32 * D;
+  if (ROT == 0 && !QROT) {
+    const int r0 = q0 + wave * 32;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+      const int P = 64 * i + lane, row = P / CPR;
+      const int ch = (P % CPR) ^ (row & QSW);
+      load_lds16(qb + (int64_t)min(r0 + row, S - 1) * p.sq.s + 8 * ch, qrows + 512 * i);
+    }
+  } else {
     const uint16_t* qrow = qb + (int64_t)qc * p.sq.s;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
@@ -511,6 +526,12 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
   st.tp.store(lds, kb, p.sk.s, kt_lo * BN, S, a.rd, a.rope);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (ROT == 0 && !QROT) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      st.qreg[c] = qi < S ? lds_read8(qrows + ql * D + 8 * ((2 * c + hh) ^ (ql & QSW))) : elem8{};
+    __syncthreads();  // every wave has its Q~ before the first fetch reuses the buffer
+  }
 
   st.sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
   st.c2 = a.scale_log2;
@@ -538,17 +559,35 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
           for (int e = 0; e < 4; ++e) w[e] = st.oacc[db][4 * a4 + e] * inv_l;
           *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * a4 + 4 * hh) = w;
         }
-    } else {
-      uint16_t* orow = (uint16_t*)p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s;
+    }
+  }
+  if (!p.out_f32) {
+    // o rows through LDS (the tile buffers are free after the last barrier of
+    // the loop; each wave uses its own 32 padded rows): whole rows out, 16
+    // bytes per lane, instead of 16-byte pieces of 32 rows per store.
+    constexpr int RS = D + 8;
+    uint16_t* orows = lds + wave * 32 * RS;
+    // The lane index passes through an empty asm here, so the address
+    // arithmetic below is not hoisted above the loop (where registers are
+    // scarcest).
+    int el = lane;
+    __asm__ volatile("" : "+v"(el));
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          u32x2 w;
-          w[0] = pack2(st.oacc[db][4 * a4] * inv_l, st.oacc[db][4 * a4 + 1] * inv_l);
-          w[1] = pack2(st.oacc[db][4 * a4 + 2] * inv_l, st.oacc[db][4 * a4 + 3] * inv_l);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * a4 + 4 * hh) = w;
-        }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        u32x2 w;
+        w[0] = pack2(st.oacc[db][4 * a4] * inv_l, st.oacc[db][4 * a4 + 1] * inv_l);
+        w[1] = pack2(st.oacc[db][4 * a4 + 2] * inv_l, st.oacc[db][4 * a4 + 3] * inv_l);
+        *reinterpret_cast<u32x2*>(orows + ql * RS + 32 * db + 8 * a4 + 4 * hh) = w;
+      }
+    uint16_t* ob = (uint16_t*)p.o + b * p.so.b + h * p.so.h;
+    const int r0 = q0 + wave * 32;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+      const int idx = 64 * i + el, row = idx / CPR, ch = idx % CPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(orows + row * RS + 8 * ch);
+      if (r0 + row < S) *reinterpret_cast<u32x4*>(ob + (int64_t)(r0 + row) * p.so.s + 8 * ch) = w;
     }
   }
 }

@@ -240,8 +240,11 @@ def test_backward_writes_every_element(gpu):
         assert bool(g.isfinite().all())
 
 
-def test_strided_packed_qkv_matches_contiguous(gpu):
-    """q, k, v as views of one [B, S, 3, H, D] buffer (the fused-QKV layout)."""
+@pytest.mark.parametrize("fws", [True, False], ids=["workspace", "no-workspace"])
+def test_strided_packed_qkv_matches_contiguous(gpu, fws):
+    """q, k, v as views of one [B, S, 3, H, D] buffer (the fused-QKV layout):
+    bit-identical to contiguous inputs through the same kernels, and within
+    the bars of the oracle on every head."""
     torch = gpu
     import causal_attention_neox_amd as neox
     wl = pu.small_workload(2, 4, 190, 64, 16, seed=13)
@@ -251,10 +254,12 @@ def test_strided_packed_qkv_matches_contiguous(gpu):
     packed = torch.stack([q, k, v], dim=0).permute(1, 3, 0, 2, 4).contiguous()  # [B,S,3,H,D]
     qs, ks, vs = (packed[:, :, i].permute(0, 2, 1, 3) for i in range(3))
     assert qs.stride(3) == 1 and not qs.is_contiguous()
-    ref = pu.run_library(inp, backward=True)
+    ref = pu.run_library(inp, backward=True, fwd_workspace=fws)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=16)
+    fw = (torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                      device="cuda") if fws else None)
+    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=16, workspace=fw)
     grads = [torch.empty_like(q) for _ in range(3)]
     ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                      device="cuda")
@@ -265,14 +270,20 @@ def test_strided_packed_qkv_matches_contiguous(gpu):
     assert torch.equal(grads[1].view(torch.int16), ref["dk"].view(torch.int16))
     assert torch.equal(grads[2].view(torch.int16), ref["dv"].view(torch.int16))
     assert torch.equal(grads[0].view(torch.int16), ref["dq"].view(torch.int16))  # deterministic
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    got = {"o": o, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
+    pu.compare(got, pu.oracle_heads(inp, heads), heads, "bf16", label=f"[B,S,3,H,D] views fws={fws}")
 
 
-def test_neox_fused_qkv_layout_through_strides(gpu):
+@pytest.mark.parametrize("fws", [True, False], ids=["workspace", "no-workspace"])
+def test_neox_fused_qkv_layout_through_strides(gpu, fws):
     """q, k, v read in place from NeoX's fused projection output, per token
     [heads, 3, head_dim] (the FT guide's QKV weight layout [hidden, 3, heads,
     head] is the converted form of HF's [hidden, heads, 3, head]): a
     [B, S, H, 3, D] buffer, head stride 3 D, sequence stride 3 H D.  Gradients
-    are written into the same interleaved layout."""
+    are written into the same interleaved layout.  Bit-identical to contiguous
+    inputs through the same kernels, and within the bars of the oracle on
+    every head."""
     torch = gpu
     import causal_attention_neox_amd as neox
     wl = pu.small_workload(2, 3, 257, 96, 24, seed=17)
@@ -282,12 +293,12 @@ def test_neox_fused_qkv_layout_through_strides(gpu):
     packed = torch.stack([q, k, v], dim=0).permute(1, 3, 2, 0, 4).contiguous()  # [B,S,H,3,D]
     qs, ks, vs = (packed[:, :, :, i].permute(0, 2, 1, 3) for i in range(3))
     assert qs.stride() == (S * H * 3 * D, 3 * D, H * 3 * D, 1)
-    ref = pu.run_library(inp, backward=True)
+    ref = pu.run_library(inp, backward=True, fwd_workspace=fws)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
-                      device="cuda")
-    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=24, workspace=fws)
+    fw = (torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                      device="cuda") if fws else None)
+    neox.neox_attn_fwd_ex(qs, ks, vs, o, lse, rotary_dim=24, workspace=fw)
     gpacked = torch.full_like(packed, float("nan"))
     gq, gk, gv = (gpacked[:, :, :, i].permute(0, 2, 1, 3) for i in range(3))
     ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
@@ -298,6 +309,10 @@ def test_neox_fused_qkv_layout_through_strides(gpu):
     assert torch.equal(lse, ref["lse"])
     for g, name in ((gq, "dq"), (gk, "dk"), (gv, "dv")):
         assert torch.equal(g.contiguous().view(torch.int16), ref[name].view(torch.int16)), name
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    got = {"o": o, "lse": lse, "dq": gq.contiguous(), "dk": gk.contiguous(),
+           "dv": gv.contiguous()}
+    pu.compare(got, pu.oracle_heads(inp, heads), heads, "bf16", label=f"[B,S,H,3,D] views fws={fws}")
 
 
 def test_fp32_outputs_option(gpu):
