@@ -3,6 +3,10 @@ and compare against the CPU oracle."""
 
 from __future__ import annotations
 
+import concurrent.futures
+import multiprocessing
+import os
+
 import numpy as np
 
 import causal_attention_neox_amd as neox
@@ -147,3 +151,91 @@ def small_workload(B, H, S, D, rd, dtype="bf16", causal=True, alibi=False, docs=
                     dtype=dtype, causal=causal, alibi=alibi, packed_docs=docs is not None,
                     doc_min=docs[0] if docs else 64, doc_max=docs[1] if docs else 4096, seed=seed,
                     amp=amp)
+
+
+# ---------------------------------------------------------------- many heads
+
+def _oracle_one_head(args):
+    """One head through the oracle in a worker process (float64 inputs)."""
+    q, k, v, do, kw, backward = args
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):  # one core per worker process
+        if backward:
+            return tuple(x[0, 0] for x in orc.attn_bwd(q, k, v, do, **kw))
+        return tuple(x[0, 0] for x in orc.attn_fwd(q, k, v, **kw))
+
+
+def _head_args(inp: Inputs, b: int, h: int, backward: bool):
+    wl = inp.wl
+    slopes = orc.alibi_slopes(wl.H) if wl.alibi else None
+    kw = dict(rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
+              softmax_scale=wl.softmax_scale, rope_doc_positions=wl.rope_doc_positions,
+              alibi=False if slopes is None else slopes[h:h + 1],
+              doc_offsets=None if inp.doc_offsets is None else inp.doc_offsets[b:b + 1])
+    sel = lambda name: _widen(inp, name, b, h)[None, None]  # noqa: E731
+    return (sel("q"), sel("k"), sel("v"), sel("dout") if backward else None, kw, backward)
+
+
+def oracle_workers(S: int) -> int:
+    """Worker processes for the oracle: the host's cores, at most 16 (the share
+    of one GPU on the test machines), fewer for long sequences (each head holds
+    several S x S float64 matrices)."""
+    n = min(16, os.cpu_count() or 1)
+    if S > 8192:
+        n = min(n, 4)
+    return max(1, n)
+
+
+def compare_many_heads(gpu: dict, inp: Inputs, heads, dtype: str, label: str = "",
+                       backward: bool = True, out_f32_bars: bool = False):
+    """Every listed head of the GPU outputs against the oracle, computed in
+    parallel worker processes (spawned: the GPU context is not inherited) and
+    compared as each head arrives; returns the stats dict of compare().
+    The bars are those of `dtype`."""
+    names = ("o", "lse", "dq", "dk", "dv") if backward else ("o", "lse")
+    g = {n: to_f64(gpu[n]) for n in names}  # one host copy of every output
+    tol = TOL[dtype]
+    mx = {n: 0.0 for n in names}
+    sm = {n: 0.0 for n in names}
+    cnt = {n: 0 for n in names}
+    refmax = {n: 0.0 for n in names}
+    worst = {}
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=oracle_workers(inp.wl.S),
+                                                mp_context=ctx) as ex:
+        futs = {ex.submit(_oracle_one_head, _head_args(inp, b, h, backward)): (b, h)
+                for b, h in heads}
+        for fut in concurrent.futures.as_completed(futs):
+            b, h = futs[fut]
+            ref = fut.result()
+            for n, r in zip(names, ref):
+                x = g[n][b, h]
+                assert np.all(np.isfinite(x)), f"{label}: non-finite {n} at head {(b, h)}"
+                err = np.abs(x - r)
+                m = float(err.max())
+                if m > mx[n]:
+                    mx[n] = m
+                    worst[n] = (b, h) + tuple(int(i) for i in np.unravel_index(int(err.argmax()), err.shape))
+                sm[n] += float(err.sum())
+                cnt[n] += err.size
+                refmax[n] = max(refmax[n], float(np.abs(r).max()))
+    stats = {n: (mx[n], sm[n] / cnt[n], refmax[n]) for n in names}
+    line = " ".join(f"{k}=({v[0]:.2e},{v[1]:.2e},|ref|max {v[2]:.2f})" for k, v in stats.items())
+    print(f"[parity] {label} ({len(heads)} heads) {line}", flush=True)
+    failures = [f"{n}: max_abs {stats[n][0]:.3e} mean_abs {stats[n][1]:.3e} worst at {worst.get(n)}"
+                for n in names
+                if stats[n][0] > tol["max_abs"] or (n != "lse" and stats[n][1] > tol["mean_abs"])]
+    assert not failures, f"{label}: " + "; ".join(failures)
+    return stats
+
+
+def spread_heads(B: int, H: int, n: int):
+    """n heads (b, h) spread over the B*H heads so that every residue of the
+    flat head index modulo 8 (the XCD a head's workgroups run on) appears, and
+    the first and last heads are included."""
+    BH = B * H
+    if n >= BH:
+        return [(i // H, i % H) for i in range(BH)]
+    idx = sorted(set([0, BH - 1] + [int(round(j * (BH - 1) / (n - 1))) for j in range(n)] +
+                     [x for x in range(8) if x < BH]))
+    return [(i // H, i % H) for i in idx]
