@@ -109,6 +109,7 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     pos = neox.NEOX_POS_ALIBI if wl.alibi else neox.NEOX_POS_ROPE
     kw = dict(pos=pos, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
               softmax_scale=wl.softmax_scale, doc_offsets=docs)
+    neox.neox_rope_table_prepare(S, kw["rotary_dim"], wl.rope_base)
 
     def step(ev):
         neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=ws, phase_events=ev[0:3], **kw)
@@ -150,6 +151,7 @@ def fwd_target(args, torch, np, neox, W):
     fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                       device="cuda")
     n = max(args.steps, 20)
+    neox.neox_rope_table_prepare(S, wl.rotary_dim, wl.rope_base)
     call = lambda ev=None: neox.neox_attn_fwd_ex(  # noqa: E731
         q, k, v, o, lse, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=True,
         softmax_scale=wl.softmax_scale, workspace=fws, phase_events=ev)
@@ -242,6 +244,7 @@ def decode(args, torch, np, neox, W):
     lse = torch.empty((wl.B, wl.H), dtype=torch.float32, device="cuda")
     ws = torch.empty(neox.neox_rope_attn_decode_workspace_size(wl.B, wl.H, wl.D, wl.cap),
                      dtype=torch.uint8, device="cuda")
+    neox.neox_rope_table_prepare(wl.cap, wl.rotary_dim, wl.rope_base)
     call = lambda i: neox.neox_rope_attn_decode(  # noqa: E731
         q, k, v, caches[i & 1][0], caches[i & 1][1], lens, o, lse, wl.rotary_dim, wl.rope_base,
         wl.softmax_scale, workspace=ws)

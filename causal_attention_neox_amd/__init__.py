@@ -7,8 +7,11 @@ functions below carry the C names, take torch tensors that already live on
 the GPU, and only marshal pointers, sizes and the current stream.  PyTorch
 supplies device memory and streams; no step of the attention runs in it.
 
-``attention()`` wraps the forward and backward calls in a torch autograd
-Function for convenience.
+The compute calls allocate nothing: a RoPE call with rotary_dim > 0 needs the
+rotary table prepared first with ``neox_rope_table_prepare(max_S, rotary_dim,
+rope_base)`` (else NeoxError with NEOX_E_NOT_PREPARED).  ``attention()`` wraps
+the forward and backward calls in a torch autograd Function and prepares the
+table itself.
 """
 
 from __future__ import annotations
@@ -256,6 +259,8 @@ def neox_check_doc_offsets(offsets_host, S: int) -> int:
 
 
 def neox_rope_table_prepare(max_S: int, rotary_dim: int, rope_base: float = 10000.0) -> None:
+    """Set-up call: builds the rotary table of the current device for positions
+    0..max_S-1 (allocates and waits; not under stream capture)."""
     _check(_lib.load().neox_rope_table_prepare(int(max_S), int(rotary_dim), float(rope_base)),
            "neox_rope_table_prepare")
 

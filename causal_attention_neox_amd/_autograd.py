@@ -9,7 +9,8 @@ from __future__ import annotations
 import torch
 
 from . import (NEOX_POS_ALIBI, NEOX_POS_ROPE, neox_attn_bwd_ex, neox_attn_fwd_ex,
-               neox_rope_attn_bwd_workspace_size, neox_rope_attn_fwd_workspace_size)
+               neox_rope_attn_bwd_workspace_size, neox_rope_attn_fwd_workspace_size,
+               neox_rope_table_prepare)
 
 
 class NeoxAttentionFn(torch.autograd.Function):
@@ -23,6 +24,9 @@ class NeoxAttentionFn(torch.autograd.Function):
         kw = dict(pos=pos, rotary_dim=rotary_dim, rope_base=rope_base, alibi_slopes=alibi_slopes,
                   causal=causal, softmax_scale=softmax_scale, doc_offsets=doc_offsets)
         ws = None
+        if rotary_dim > 0 and not alibi:
+            with torch.cuda.device(q.device):
+                neox_rope_table_prepare(S, rotary_dim, rope_base)
         if rotary_dim > 0 and not alibi and q.dtype in (torch.bfloat16, torch.float16):
             ws = torch.empty(neox_rope_attn_fwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                              device=q.device)

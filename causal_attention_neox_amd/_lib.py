@@ -20,6 +20,7 @@ NEOX_E_WORKSPACE = -4
 NEOX_E_LAUNCH = -5
 NEOX_E_DEVICE = -6
 NEOX_E_ALLOC = -7
+NEOX_E_NOT_PREPARED = -8
 
 NEOX_F32 = 0
 NEOX_BF16 = 1

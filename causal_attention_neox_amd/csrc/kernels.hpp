@@ -118,9 +118,6 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st, const hipEvent_t*
 hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t st, const hipEvent_t* ev);
 
-// dq = dq_scale * R^T dQ~ from the fp32 accumulator, cast; shared by both paths
-// (the bf16 path accumulates dS without the softmax scale and passes it here).
-
 inline hipError_t record_event(const hipEvent_t* ev, int i, hipStream_t st) {
   return ev ? hipEventRecord(ev[i], st) : hipSuccess;
 }

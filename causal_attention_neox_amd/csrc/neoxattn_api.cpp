@@ -64,10 +64,10 @@ uint32_t float_bits(float f) {
   return u;
 }
 
-// Returns a table covering positions 0..S-1.  A new table is built on `st` and
-// waited for; under stream capture that is impossible, so the caller gets
-// NEOX_E_ALLOC and must call neox_rope_table_prepare() first.
-int get_rope_table(int dev, int S, int rd, float base, hipStream_t st, const float2** out) {
+// The prepared table of this device covering positions 0..S-1, or
+// NEOX_E_NOT_PREPARED.  Compute calls only look tables up: they never
+// allocate or wait.
+int find_rope_table(int dev, int S, int rd, float base, const float2** out) {
   std::lock_guard<std::mutex> lk(g_mu);
   const uint32_t bb = float_bits(base);
   for (const RopeTable& t : g_tables) {
@@ -76,14 +76,24 @@ int get_rope_table(int dev, int S, int rd, float base, hipStream_t st, const flo
       return NEOX_OK;
     }
   }
-  if (st != nullptr) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NEOX_E_DEVICE;
-    if (cs != hipStreamCaptureStatusNone) return NEOX_E_ALLOC;
-  }
+  return NEOX_E_NOT_PREPARED;
+}
+
+// Builds (allocating) a table covering at least positions 0..S-1 on the null
+// stream and waits for it; called by neox_rope_table_prepare only.
+int build_rope_table(int dev, int S, int rd, float base, const float2** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const uint32_t bb = float_bits(base);
+  hipStream_t st = nullptr;
   int cap = S;
-  for (const RopeTable& t : g_tables)
-    if (t.dev == dev && t.rd == rd && t.base_bits == bb && 2 * t.cap > cap) cap = 2 * t.cap;
+  for (const RopeTable& t : g_tables) {
+    if (t.dev != dev || t.rd != rd || t.base_bits != bb) continue;
+    if (t.cap >= S) {
+      *out = t.ptr;
+      return NEOX_OK;
+    }
+    if (2 * t.cap > cap) cap = 2 * t.cap;
+  }
   cap = (cap + 255) & ~255;
   float2* ptr = nullptr;
   if (hipMalloc(&ptr, (size_t)cap * (size_t)(rd / 2) * sizeof(float2)) != hipSuccess) {
@@ -162,17 +172,18 @@ int fill_shape(const neox_attn_args* a, const float2* rope, neox::AttnShape* sh)
   return NEOX_OK;
 }
 
-int prepare_rope(const neox_attn_args* a, int dev, hipStream_t st, const float2** rope) {
+int lookup_rope(const neox_attn_args* a, int dev, const float2** rope) {
   *rope = nullptr;
   if (a->pos == NEOX_POS_ROPE && a->rotary_dim > 0)
-    return get_rope_table(dev, a->S, a->rotary_dim, a->rope_base, st, rope);
+    return find_rope_table(dev, a->S, a->rotary_dim, a->rope_base, rope);
   return NEOX_OK;
 }
 
 // Backward workspace: the rotated 16-bit q and k [rows][D] each (first, at the
-// offsets the forward workspace uses, so one buffer can serve both calls), the
-// fp32 dq accumulator [rows][D], fp32 Delta [rows] and fp32 -lse*log2e [rows];
-// 256-byte aligned pieces, rows = B*H*S.
+// offsets the forward workspace uses, so one buffer can serve both calls; used
+// by the 16-bit paths) or, over the same bytes, the fp32 dq accumulator
+// [rows][D] (used by the fp32 path only); then fp32 Delta [rows] and fp32
+// -lse*log2e [rows]; 256-byte aligned pieces, rows = B*H*S.
 struct BwdWorkspace {
   size_t dq_acc, delta, nlse, qrot, krot, total;
 };
@@ -183,11 +194,12 @@ bool bwd_workspace_layout(int B, int H, int S, int D, BwdWorkspace* w) {
   if (rows >= kMaxRows || D > 4096) return false;
   size_t off = 0;
   w->qrot = off;
+  w->dq_acc = off;
   off += round256((size_t)rows * (size_t)D * 2u);
   w->krot = off;
   off += round256((size_t)rows * (size_t)D * 2u);
-  w->dq_acc = off;
-  off += round256((size_t)rows * (size_t)D * 4u);
+  const size_t acc_end = round256((size_t)rows * (size_t)D * 4u);
+  if (acc_end > off) off = acc_end;
   w->delta = off;
   off += round256((size_t)rows * 4u);
   w->nlse = off;
@@ -230,7 +242,10 @@ const char* neox_status_str(int status) {
     case NEOX_E_WORKSPACE: return "workspace missing or too small";
     case NEOX_E_LAUNCH: return "kernel launch failed";
     case NEOX_E_DEVICE: return "no usable gfx950 device or HIP runtime error";
-    case NEOX_E_ALLOC: return "rotary table allocation failed or not prepared under capture";
+    case NEOX_E_ALLOC: return "rotary table allocation failed";
+    case NEOX_E_NOT_PREPARED:
+      return "rotary table not prepared for this rotary_dim, rope_base and length "
+             "(call neox_rope_table_prepare first)";
     default: return "unknown status";
   }
 }
@@ -261,7 +276,7 @@ int neox_attn_fwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   if ((st = check_device(&dev)) != NEOX_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
-  if ((st = prepare_rope(a, dev, hs, &rope)) != NEOX_OK) return st;
+  if ((st = lookup_rope(a, dev, &rope)) != NEOX_OK) return st;
 
   neox::FwdParams p;
   fill_shape(a, rope, &p.a);
@@ -322,7 +337,7 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   if ((st = check_device(&dev)) != NEOX_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
-  if ((st = prepare_rope(a, dev, hs, &rope)) != NEOX_OK) return st;
+  if ((st = lookup_rope(a, dev, &rope)) != NEOX_OK) return st;
 
   neox::BwdParams p;
   fill_shape(a, rope, &p.a);
@@ -430,7 +445,7 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   if (st != NEOX_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
-  if (rotary_dim > 0 && (st = get_rope_table(dev, cap, rotary_dim, rope_base, hs, &rope)) != NEOX_OK)
+  if (rotary_dim > 0 && (st = find_rope_table(dev, cap, rotary_dim, rope_base, &rope)) != NEOX_OK)
     return st;
 
   neox::DecodeParams p;
@@ -511,7 +526,7 @@ int neox_rope_table_prepare(int max_S, int rotary_dim, float rope_base) {
   int st = check_device(&dev);
   if (st != NEOX_OK) return st;
   const float2* rope = nullptr;
-  return get_rope_table(dev, max_S, rotary_dim, rope_base, nullptr, &rope);
+  return build_rope_table(dev, max_S, rotary_dim, rope_base, &rope);
 }
 
 }  // extern "C"

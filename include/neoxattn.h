@@ -42,12 +42,17 @@
  *    rope_base > 0 and finite; softmax_scale > 0 and finite; B, H, S >= 1;
  *    B*H*S < 2^31; tensor base pointers 16-byte aligned; row strides multiples
  *    of 8 elements (bf16, fp16) or 4 elements (fp32).
- *  - Rotary cos/sin table: the first call on a device for a (rotary_dim,
- *    rope_base) pair, or for a longer S than that pair has seen, allocates a
- *    table of S * rotary_dim * 4 bytes on the device and fills it (angles and
- *    cos/sin in double, stored as fp32).  Tables live until the process ends.
- *    neox_rope_table_prepare() builds one ahead of time, so that later calls
- *    allocate nothing.
+ *  - The compute calls (forward, backward, decode, FP8 forward) allocate
+ *    nothing and never wait: every buffer is the caller's, and the rotary
+ *    cos/sin table of a (rotary_dim, rope_base) pair -- the per-layer
+ *    inv_freq buffer of the checkpoint ("FasterTransformer GPT-NeoX 推理指南",
+ *    the attention.rotary_emb.inv_freq tensor of the converted model) turned
+ *    into cos/sin of t * inv_freq -- must have been built beforehand by
+ *    neox_rope_table_prepare() on the calling device for at least the
+ *    sequence length (the decode cache capacity) of the call.  A call that
+ *    needs a table that has not been prepared returns NEOX_E_NOT_PREPARED
+ *    and enqueues nothing.  Calls with rotary_dim = 0, ALiBi or no position
+ *    scheme need no table.
  */
 #ifndef NEOXATTN_H
 #define NEOXATTN_H
@@ -67,7 +72,8 @@ extern "C" {
 #define NEOX_E_WORKSPACE (-4)   /* workspace NULL or smaller than required */
 #define NEOX_E_LAUNCH (-5)      /* a kernel launch failed */
 #define NEOX_E_DEVICE (-6)      /* no usable gfx950 device / HIP runtime error */
-#define NEOX_E_ALLOC (-7)       /* rotary table allocation failed */
+#define NEOX_E_ALLOC (-7)       /* rotary table allocation failed (neox_rope_table_prepare) */
+#define NEOX_E_NOT_PREPARED (-8) /* rotary table not prepared: call neox_rope_table_prepare */
 
 /* Storage type of q, k, v, o, dout (and of dq, dk, dv unless out_dtype says fp32). */
 #define NEOX_F32 0
@@ -142,7 +148,8 @@ typedef struct neox_attn_args {
   int reuse_rotated_qk;
 } neox_attn_args;
 
-/* Text of a status code (static storage, never NULL). */
+/* Text of a status code (static storage, never NULL).  The codes name the
+ * argument rules stated above. */
 const char* neox_status_str(int status);
 
 /*
@@ -174,25 +181,35 @@ int neox_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int causal, float softmax_scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace the backward needs, in five 256-byte aligned
- * parts: the rotated q and k in the 16-bit storage type, [B, H, S, D] each
- * (used by the bf16 and fp16 paths only; placed first, exactly where the
- * forward workspace holds them, so a backward workspace also serves as the
- * forward's -- see reuse_rotated_qk), an fp32 [B, H, S, D] dq accumulator (fp32
- * path) and two fp32 [B, H, S] row terms (the softmax-gradient row sum and the
- * negated base-2 log-sum-exp); the size does not depend on dtype --
- * B*H*S*(8D + 8) bytes up to rounding, linear in S.  Returns 0 for sizes that are invalid (<= 0) or overflow. */
+/* Bytes of device workspace the backward needs.  The backward recomputes the
+ * probabilities from lse instead of storing the S x S matrix -- the O(n)
+ * memory of the tiled form ("GPT-NeoX 开源训练框架深度解读", section
+ * "问题二：注意力计算太慢") -- so the workspace is linear in S: the rotated q
+ * and k in the 16-bit storage type, [B, H, S, D] each (bf16 and fp16 paths;
+ * placed first, exactly where the forward workspace holds them, so a
+ * backward workspace also serves as the forward's -- see reuse_rotated_qk),
+ * or over the same bytes an fp32 [B, H, S, D] dq accumulator (fp32 path),
+ * then two fp32 [B, H, S] row terms (the softmax-gradient row sum and the
+ * negated base-2 log-sum-exp); 256-byte aligned parts, B*H*S*(4D + 8) bytes
+ * up to rounding for every dtype.  Returns 0 for sizes that are invalid
+ * (<= 0) or overflow. */
 size_t neox_rope_attn_bwd_workspace_size(int B, int H, int S, int D);
 
 /*
- * Backward.  Inputs q, k, v, o, dout ([B, H, S, D], `dtype`) and lse (from the
- * forward with the same arguments) are read only.  dq, dk, dv ([B, H, S, D],
- * `dtype`) are written and must not alias the inputs.  workspace: device
- * memory of at least neox_rope_attn_bwd_workspace_size() bytes, 256-byte
- * aligned, owned by the caller, overwritten by the call (its contents
- * afterwards are unspecified).  The bf16 and fp16 paths are deterministic (dq,
- * dk and dv are each reduced by one workgroup, in a fixed order); the fp32 path
- * accumulates dq with fp32 atomics, so its last bits may vary run to run.
+ * Backward of the same attention (the pages' subject is training GPT-NeoX with
+ * this attention: "GPT-NeoX 开源训练框架深度解读", section "问题二：注意力计算
+ * 太慢").  With P_ij = exp(s_ij - lse_i), dP_ij = dout_i . v_j,
+ * Delta_i = dout_i . o_i and dS_ij = P_ij (dP_ij - Delta_i):
+ *     dv_j = sum_i P_ij dout_i
+ *     dq_i = R_i^T softmax_scale sum_j dS_ij k~_j
+ *     dk_j = R_j^T softmax_scale sum_i dS_ij q~_i
+ * Inputs q, k, v, o, dout ([B, H, S, D], `dtype`) and lse (from the forward
+ * with the same arguments) are read only.  dq, dk, dv ([B, H, S, D], `dtype`)
+ * are written and must not alias the inputs.  workspace: device memory of at
+ * least neox_rope_attn_bwd_workspace_size() bytes, 256-byte aligned, owned by
+ * the caller, overwritten by the call (its contents afterwards are
+ * unspecified).  Deterministic for every dtype: dq, dk and dv are each reduced
+ * by one workgroup in a fixed order (no atomics).
  */
 int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -200,13 +217,17 @@ int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int causal, float softmax_scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Forward with ALiBi, packed documents, strides and output type (see
+/* Forward with ALiBi (the pages' alternative position scheme, "GPT-NeoX 开源训练
+ * 框架深度解读", section "架构创新"), packed documents, strides (NeoX's fused
+ * per-head [heads, 3, head_dim] QKV read in place, "FasterTransformer GPT-NeoX
+ * 推理指南", the QKV weight conversion step) and output type (see
  * neox_attn_args); workspace as for neox_rope_attn_fwd. */
 int neox_attn_fwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,
                      void* o, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
 
-/* Backward counterpart of neox_attn_fwd_ex; workspace as for neox_rope_attn_bwd. */
+/* Backward counterpart of neox_attn_fwd_ex (same passages as neox_attn_fwd_ex
+ * and neox_rope_attn_bwd); workspace as for neox_rope_attn_bwd. */
 int neox_attn_bwd_ex(const neox_attn_args* args, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, void* stream);
@@ -246,9 +267,10 @@ size_t neox_rope_attn_decode_workspace_size(int B, int H, int D, int cap);
  *               neox_rope_attn_decode_workspace_size(B, H, D, cap) bytes,
  *               256-byte aligned, owned by the caller, overwritten.
  * Supported: D in {64, 96, 128}; cap >= 1; B*H*cap < 2^31; 0 <= rotary_dim
- * <= D, even; pointers 16-byte aligned.  The rotary table covers positions
- * 0 .. cap - 1 (allocated as described above).  Same status codes as the
- * other entry points; o and lse must not alias the inputs or the cache.
+ * <= D, even; pointers 16-byte aligned.  The rotary table must cover
+ * positions 0 .. cap - 1 (neox_rope_table_prepare(cap, ...)).  Same status
+ * codes as the other entry points; o and lse must not alias the inputs or
+ * the cache.
  */
 int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_cache,
                           void* v_cache, const int32_t* cache_lens, void* o, float* lse,
@@ -278,17 +300,25 @@ int neox_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_sc
                       int D, int causal, float softmax_scale, int out_dtype, void* stream);
 
 /*
- * Host-side check of a HOST copy of doc_offsets ([B][n_docs + 1] int32):
+ * Host-side check of a HOST copy of doc_offsets ([B][n_docs + 1] int32), the
+ * packed-document layout of neox_attn_args (documents packed into one
+ * sequence, no attention across them; the pages leave packing open, the
+ * document boundaries come with the workload):
  * returns NEOX_OK when every row starts at 0, never decreases and ends at S,
  * NEOX_E_ARG otherwise (or for a NULL pointer / bad sizes).  No device work.
  */
 int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S);
 
 /*
- * Builds (allocating if needed) the rotary cos/sin table of the current
- * device for positions 0..max_S-1, rotary_dim and rope_base, and waits for it.
- * Later calls with S <= max_S and the same pair allocate nothing.  Returns
- * NEOX_OK, NEOX_E_ARG, NEOX_E_ALLOC or NEOX_E_DEVICE.
+ * Set-up call: builds the rotary cos/sin table of the current device for
+ * positions 0..max_S-1, rotary_dim and rope_base (the checkpoint's
+ * attention.rotary_emb.inv_freq, "FasterTransformer GPT-NeoX 推理指南", as
+ * cos/sin of t * base^(-2p / rotary_dim), computed in double and stored as
+ * fp32), allocating about max_S * rotary_dim * 4 bytes of device memory, and waits for
+ * it.  Tables live until the process ends; compute calls with S <= max_S and
+ * the same pair then find it.  Not to be called under stream capture.
+ * Returns NEOX_OK (also when a covering table exists), NEOX_E_ARG,
+ * NEOX_E_ALLOC, NEOX_E_LAUNCH or NEOX_E_DEVICE.
  */
 int neox_rope_table_prepare(int max_S, int rotary_dim, float rope_base);
 

@@ -57,6 +57,8 @@ def run_library(inp: Inputs, backward: bool = True, out_f32: bool = False, force
     kw = dict(pos=pos, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base, causal=wl.causal,
               softmax_scale=wl.softmax_scale, doc_offsets=docs, out_f32=out_f32)
     B, H, S, D = q.shape
+    if not wl.alibi:
+        neox.neox_rope_table_prepare(S, wl.rotary_dim, wl.rope_base)
     fws = None
     ws = torch.empty(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
                      device="cuda")

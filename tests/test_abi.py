@@ -19,6 +19,7 @@ from causal_attention_neox_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, E_ARG, E_UNSUP, E_ALIGN, E_WS, E_LAUNCH, E_DEV, E_ALLOC = 0, -1, -2, -3, -4, -5, -6, -7
+E_NOT_PREPARED = -8
 F32, BF16 = 0, 1
 P = ctypes.c_void_p
 A1, A2, A3, A4, A5, A6, A7, A8, A9 = (P(0x10000 * n) for n in range(1, 10))  # 16-byte aligned
@@ -62,8 +63,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in (OK, E_ARG, E_UNSUP, E_ALIGN, E_WS, E_LAUNCH, E_DEV, E_ALLOC):
-        assert lib.neox_status_str(s)
+    for s in (OK, E_ARG, E_UNSUP, E_ALIGN, E_WS, E_LAUNCH, E_DEV, E_ALLOC, E_NOT_PREPARED):
+        assert lib.neox_status_str(s) != b"unknown status"
+    assert b"neox_rope_table_prepare" in lib.neox_status_str(E_NOT_PREPARED)
     assert lib.neox_status_str(OK) == b"ok"
     assert lib.neox_status_str(12345) == b"unknown status"
 
@@ -175,16 +177,23 @@ def test_valid_call_without_gpu_fails_loudly(lib):
 
 
 def test_workspace_size_is_linear_in_sequence_length(lib):
-    """O(n) memory: the backward workspace is an fp32 dq accumulator, two fp32
-    row terms and the rotated q and k (2 bytes per element), each part rounded
-    up to 256 bytes, with no S^2 term."""
+    """O(n) memory: the backward workspace is the rotated q and k (2 bytes per
+    element; the fp32 path's dq accumulator lies over the same bytes) and two
+    fp32 row terms, each part rounded up to 256 bytes, with no S^2 term: the
+    forward workspace plus 8 bytes per row."""
     def r256(n):
         return ((n + 255) // 256) * 256
-    for (B, H, D) in [(1, 1, 64), (4, 64, 96), (1, 32, 128)]:
+    for (B, H, D) in [(1, 1, 64), (4, 64, 96), (1, 32, 128), (3, 5, 96)]:
         for S in (1, 17, 2048, 16384, 1 << 20):
             rows = B * H * S
-            expect = 2 * r256(rows * D * 2) + r256(rows * D * 4) + 2 * r256(rows * 4)
+            rot = 2 * r256(rows * D * 2)
+            acc = r256(rows * D * 4)
+            assert acc <= rot  # the fp32 accumulator fits over the rotated rows
+            expect = rot + 2 * r256(rows * 4)
             assert lib.neox_rope_attn_bwd_workspace_size(B, H, S, D) == expect
+            if rows * D < (1 << 31):
+                fwd = lib.neox_rope_attn_fwd_workspace_size(B, H, S, D)
+                assert fwd == rot and expect - fwd == 2 * r256(rows * 4)
     assert lib.neox_rope_attn_bwd_workspace_size(0, 1, 1, 64) == 0
     assert lib.neox_rope_attn_bwd_workspace_size(1 << 16, 1 << 8, 1 << 8, 64) == 0
 
@@ -205,7 +214,82 @@ def test_rope_table_prepare_validation(lib):
     assert lib.neox_rope_table_prepare(0, 16, 1e4) == E_ARG
     assert lib.neox_rope_table_prepare(128, 15, 1e4) == E_ARG
     assert lib.neox_rope_table_prepare(128, 16, -1.0) == E_ARG
+    assert lib.neox_rope_table_prepare(128, -2, 1e4) == E_ARG
+    assert lib.neox_rope_table_prepare(128, 16, float("nan")) == E_ARG
     assert lib.neox_rope_table_prepare(128, 0, 1e4) == OK  # nothing to build
+    if not os.path.exists("/dev/kfd"):
+        assert lib.neox_rope_table_prepare(128, 16, 1e4) == E_DEV
+
+
+@pytest.mark.gpu
+def test_unprepared_rotary_table_is_an_error_and_enqueues_nothing(lib):
+    """Compute calls never allocate: a RoPE call whose (rotary_dim, rope_base,
+    length) has no prepared table returns NEOX_E_NOT_PREPARED before touching
+    any buffer; after neox_rope_table_prepare the same call runs.  A table
+    prepared for a longer length serves shorter ones; rotary_dim = 0 and ALiBi
+    need none."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_attention_neox_amd as neox
+    B, H, S, D, rd, base = 1, 2, 160, 64, 16, 4321.5  # a base no other test prepares
+    q, k, v, do = (torch.randn(B, H, S, D, device="cuda").to(torch.bfloat16) for _ in range(4))
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((B, H, S), 7.0, device="cuda")
+    ws = torch.zeros(neox.neox_rope_attn_bwd_workspace_size(B, H, S, D), dtype=torch.uint8,
+                     device="cuda")
+    grads = [torch.full_like(q, 7.0) for _ in range(3)]
+    dec_ws = torch.zeros(neox.neox_rope_attn_decode_workspace_size(B, H, D, S),
+                         dtype=torch.uint8, device="cuda")
+    lens = torch.full((B,), 5, dtype=torch.int32, device="cuda")
+    kc, vc = k.clone(), v.clone()
+    o1 = torch.full((B, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    l1 = torch.full((B, H), 7.0, device="cuda")
+
+    def calls(length):
+        qq, kk, vv, oo, ll, dd = (t[:, :, :length] for t in (q, k, v, o, lse, do))
+        gg = [g[:, :, :length] for g in grads]
+        with pytest.raises(neox.NeoxError) as e1:
+            neox.neox_rope_attn_fwd(qq, kk, vv, oo, ll, rd, base, workspace=ws)
+        with pytest.raises(neox.NeoxError) as e2:
+            neox.neox_attn_fwd_ex(qq, kk, vv, oo, ll, rotary_dim=rd, rope_base=base)
+        with pytest.raises(neox.NeoxError) as e3:
+            neox.neox_rope_attn_bwd(qq, kk, vv, oo, dd, ll, *gg, rd, base, workspace=ws)
+        with pytest.raises(neox.NeoxError) as e4:
+            neox.neox_attn_bwd_ex(qq, kk, vv, oo, dd, ll, *gg, rotary_dim=rd, rope_base=base,
+                                  workspace=ws)
+        return [e.value.status for e in (e1, e2, e3, e4)]
+
+    torch.cuda.synchronize()
+    assert calls(S) == [E_NOT_PREPARED] * 4
+    with pytest.raises(neox.NeoxError) as e5:
+        neox.neox_rope_attn_decode(*(t[:, :, 0].contiguous() for t in (q, k, v)), kc, vc, lens,
+                                   o1, l1, rd, base, workspace=dec_ws)
+    assert e5.value.status == E_NOT_PREPARED
+    neox.neox_rope_table_prepare(S // 2, rd, base)
+    assert calls(S) == [E_NOT_PREPARED] * 4  # the table is shorter than S
+    torch.cuda.synchronize()
+    for t in [o, lse, o1, l1] + grads:
+        assert bool((t == 7.0).all()), "a refused call wrote an output"
+    assert bool((ws == 0).all()) and bool((dec_ws == 0).all())
+    assert bool(torch.equal(kc, k)) and bool(torch.equal(vc, v))
+    # a table for S covers every shorter length
+    neox.neox_rope_table_prepare(S, rd, base)
+    neox.neox_rope_table_prepare(S // 4, rd, base)  # already covered: no new table
+    for length in (S, S // 2, 33):
+        qq, kk, vv = (t[:, :, :length].contiguous() for t in (q, k, v))
+        oo = torch.empty_like(qq)
+        ll = torch.empty((B, H, length), device="cuda")
+        neox.neox_attn_fwd_ex(qq, kk, vv, oo, ll, rotary_dim=rd, rope_base=base)
+        torch.cuda.synchronize()
+        assert bool(oo.isfinite().all()) and bool(ll.isfinite().all())
+    q1, k1, v1 = (t[:, :, 0].contiguous() for t in (q, k, v))
+    neox.neox_rope_attn_decode(q1, k1, v1, kc, vc, lens, o1, l1, rd, base, workspace=dec_ws)
+    # no table needed without rotation or with ALiBi
+    neox.neox_attn_fwd_ex(q, k, v, o, lse, rotary_dim=0, rope_base=base)
+    neox.neox_attn_fwd_ex(q, k, v, o, lse, pos=neox.NEOX_POS_ALIBI)
+    torch.cuda.synchronize()
+    assert bool(o.isfinite().all()) and bool(o1.isfinite().all())
 
 
 def test_generated_doc_layout_is_valid(lib):

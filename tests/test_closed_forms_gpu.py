@@ -181,6 +181,7 @@ def test_outputs_leave_canary_bands_untouched(gpu, case):
     ws = ws_buf[:wsz]
     pos = neox.NEOX_POS_ALIBI if alibi else neox.NEOX_POS_ROPE
     kw = dict(pos=pos, rotary_dim=0 if alibi else rd)
+    neox.neox_rope_table_prepare(S, kw["rotary_dim"])
     neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=ws, **kw)
     neox.neox_attn_bwd_ex(q, k, v, o, do, lse, grads[0][1], grads[1][1], grads[2][1],
                           workspace=ws, reuse_rotated_qk=not alibi, **kw)

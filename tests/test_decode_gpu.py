@@ -73,6 +73,7 @@ def _run(torch, neox, wl, q, k, v, kc, vc, lens, stream=None):
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(neox.neox_rope_attn_decode_workspace_size(B, H, D, cap), dtype=torch.uint8,
                      device="cuda")
+    neox.neox_rope_table_prepare(cap, wl.rotary_dim, wl.rope_base)
     neox.neox_rope_attn_decode(q, k, v, kc, vc, lens, o, lse, wl.rotary_dim, wl.rope_base,
                                wl.softmax_scale, workspace=ws)
     return o, lse

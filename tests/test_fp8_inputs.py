@@ -37,3 +37,17 @@ def test_generated_fp8_inputs_use_the_full_range():
         v = orc.e4m3_decode(codes)
         assert np.abs(v).max() == 448.0           # amax maps to the largest code
         assert np.all(np.isfinite(v)) and scale > 0
+
+
+def test_encoding_matches_torch_float8_e4m3fn():
+    """Independent check of the rounding: torch's float8_e4m3fn cast (the same
+    OCP format) gives the same codes on 2e5 float32 samples across the whole
+    finite range, subnormals included (|x| <= 448: torch's cast does not
+    saturate)."""
+    torch = __import__("pytest").importorskip("torch")
+    rng = np.random.default_rng(2026)
+    mag = np.exp2(rng.uniform(-12.0, np.log2(448.0), 200_000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    x[:1000] = np.minimum(np.abs(x[:1000]), 448.0)  # some values at the top binade
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(W.e4m3_encode(x.astype(np.float64)), ref)

@@ -227,6 +227,8 @@ def test_forward_is_deterministic_and_writes_every_element(gpu):
     wl = pu.small_workload(2, 3, 333, 128, 128, seed=11)
     inp = generate(wl, with_dout=False)
     q, k, v = (pu.to_device(inp, n) for n in ("q", "k", "v"))
+    import causal_attention_neox_amd as neox
+    neox.neox_rope_table_prepare(333, 128)
     outs = []
     for _ in range(3):
         o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
@@ -276,6 +278,7 @@ def test_backward_writes_every_element(gpu):
     q, k, v, do = (pu.to_device(inp, n) for n in ("q", "k", "v", "dout"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    neox.neox_rope_table_prepare(257, 24)
     neox.neox_rope_attn_fwd(q, k, v, o, lse, 24)
     ws = torch.full((neox.neox_rope_attn_bwd_workspace_size(1, 2, 257, 96),), 255,
                     dtype=torch.uint8, device="cuda")  # NaN-patterned workspace
