@@ -315,8 +315,9 @@ int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S
  * attention.rotary_emb.inv_freq, "FasterTransformer GPT-NeoX 推理指南", as
  * cos/sin of t * base^(-2p / rotary_dim), computed in double and stored as
  * fp32), allocating about max_S * rotary_dim * 4 bytes of device memory, and waits for
- * it.  Tables live until the process ends; compute calls with S <= max_S and
- * the same pair then find it.  Not to be called under stream capture.
+ * it (max_S is rounded up to a multiple of 256 positions).  Tables live until
+ * the process ends; compute calls with S <= max_S and the same pair then find
+ * it.  Not to be called under stream capture.
  * Returns NEOX_OK (also when a covering table exists), NEOX_E_ARG,
  * NEOX_E_ALLOC, NEOX_E_LAUNCH or NEOX_E_DEVICE.
  */

@@ -232,7 +232,9 @@ def test_unprepared_rotary_table_is_an_error_and_enqueues_nothing(lib):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import causal_attention_neox_amd as neox
-    B, H, S, D, rd, base = 1, 2, 160, 64, 16, 4321.5  # a base no other test prepares
+    # a base no other test prepares; tables are built for whole multiples of 256
+    # positions, so S // 2 = 150 gets a 256-position table, short of S = 300
+    B, H, S, D, rd, base = 1, 2, 300, 64, 16, 4321.5
     q, k, v, do = (torch.randn(B, H, S, D, device="cuda").to(torch.bfloat16) for _ in range(4))
     o = torch.full_like(q, 7.0)
     lse = torch.full((B, H, S), 7.0, device="cuda")
