@@ -92,6 +92,16 @@ def load() -> ctypes.CDLL:
                 raise RuntimeError(
                     f"{LIB_PATH} is missing: build it with `python -m causal_attention_neox_amd.build` "
                     "(or __graft_entry__.build()); there is no fallback implementation")
+            # One HIP runtime per process: torch's HIP libraries ask for the
+            # runtime as libamdhip64.so while this library asks for
+            # libamdhip64.so.7, so whichever loads first decides; loaded before
+            # torch, this library would pull in a second runtime next to
+            # torch's, and the one initialised second finds no device.  Loading
+            # torch first makes both share torch's runtime.
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             lib = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 fn = getattr(lib, name)
