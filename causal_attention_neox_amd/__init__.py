@@ -28,7 +28,8 @@ __all__ = [
     "NeoxError", "neox_status_str", "neox_rope_attn_fwd", "neox_rope_attn_bwd",
     "neox_rope_attn_fwd_workspace_size", "neox_rope_attn_bwd_workspace_size",
     "neox_attn_fwd_ex", "neox_attn_bwd_ex",
-    "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode", "neox_attn_fwd_fp8",
+    "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode",
+    "neox_rope_attn_decode_noalloc", "neox_attn_fwd_fp8",
     "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
     "NEOX_F32", "NEOX_BF16", "NEOX_F16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
@@ -229,6 +230,24 @@ def neox_rope_attn_decode(q, k, v, k_cache, v_cache, cache_lens, o, lse, rotary_
         _ptr(lse), B, H, D, cap, int(rotary_dim), float(rope_base), scale, _dtype_code(q),
         _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "neox_rope_attn_decode")
+
+
+def neox_rope_attn_decode_noalloc(q, k, v, k_cache, v_cache, cache_lens, o, lse,
+                                  rotary_dim: int, rope_base: float = 10000.0,
+                                  softmax_scale: Optional[float] = None, stream=None) -> None:
+    """Calls neox_rope_attn_decode_noalloc: as neox_rope_attn_decode, with the
+    chunk partials in the library's fixed per-device array instead of a
+    workspace (calls on one device must not overlap)."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, D] and the caches [B, H, cap, D]")
+    B, H, D = (int(x) for x in q.shape)
+    cap = int(k_cache.shape[2])
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().neox_rope_attn_decode_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(o),
+        _ptr(lse), B, H, D, cap, int(rotary_dim), float(rope_base), scale, _dtype_code(q),
+        _stream(stream))
+    _check(st, "neox_rope_attn_decode_noalloc")
 
 
 def neox_attn_fwd_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, o, lse,

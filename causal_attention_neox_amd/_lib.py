@@ -21,6 +21,8 @@ NEOX_E_LAUNCH = -5
 NEOX_E_DEVICE = -6
 NEOX_E_ALLOC = -7
 NEOX_E_NOT_PREPARED = -8
+NEOX_E_TOO_LARGE = -9
+NEOX_DECODE_SCRATCH_BYTES = 8 << 20
 
 NEOX_F32 = 0
 NEOX_BF16 = 1
@@ -72,6 +74,10 @@ SIGNATURES = {
                                       c_void_p, c_void_p, c_void_p,
                                       c_int, c_int, c_int, c_int, c_int, c_float, c_float,
                                       c_int, c_void_p, c_size_t, c_void_p]),
+    "neox_rope_attn_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p,
+                                              c_int, c_int, c_int, c_int, c_int, c_float,
+                                              c_float, c_int, c_void_p]),
     "neox_attn_fwd_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_float, c_float, c_float,
                                   c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                   c_float, c_int, c_void_p]),

@@ -27,9 +27,18 @@
 //
 // The step reads every cached key and value once, so it is bound by HBM
 // bandwidth: 2 t D element reads per (batch, head).
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
+#include "../../include/neoxattn.h"
 #include "device_common.hpp"
+
+// Chunk partials of neox_rope_attn_decode_noalloc: one fixed array in every
+// device's copy of the code object, held until the process ends.  In host code
+// this name is only a stand-in for the device address; decode_scratch() looks
+// the real one up per device, and only that pointer reaches kernels.
+static __device__ __align__(256) float scratch[NEOX_DECODE_SCRATCH_BYTES / sizeof(float)];
 
 namespace neox {
 namespace {
@@ -427,6 +436,25 @@ void decode_plan(int BH, int cap, int* chunk, int* nsplit) {
 #endif
   *chunk = c;
   *nsplit = (cap + c - 1) / c;
+}
+
+// Device address of `scratch` on device `dev`, which must be the current
+// device; looked up once per device and kept.
+hipError_t decode_scratch(int dev, float** out) {
+  static std::mutex mu;
+  static std::vector<float*> addr;  // indexed by device
+  if (dev < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((size_t)dev >= addr.size()) addr.resize((size_t)dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(ptr);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {

@@ -101,6 +101,8 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t st);
 int decode_tile_rows();
 void decode_plan(int BH, int cap, int* chunk, int* nsplit);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
+// Device address of the fixed decode scratch array on `dev` (the current device).
+hipError_t decode_scratch(int dev, float** out);
 
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
 

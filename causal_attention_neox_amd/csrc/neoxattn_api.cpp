@@ -243,6 +243,9 @@ const char* neox_status_str(int status) {
     case NEOX_E_LAUNCH: return "kernel launch failed";
     case NEOX_E_DEVICE: return "no usable gfx950 device or HIP runtime error";
     case NEOX_E_ALLOC: return "rotary table allocation failed";
+    case NEOX_E_TOO_LARGE:
+      return "problem larger than the fixed scratch of the no-allocation entry point "
+             "(NEOX_DECODE_SCRATCH_BYTES)";
     case NEOX_E_NOT_PREPARED:
       return "rotary table not prepared for this rotary_dim, rope_base and length "
              "(call neox_rope_table_prepare first)";
@@ -418,11 +421,15 @@ int neox_rope_attn_bwd(const void* q, const void* k, const void* v, const void* 
                           stream);
 }
 
-int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_cache,
-                          void* v_cache, const int32_t* cache_lens, void* o, float* lse, int B,
-                          int H, int D, int cap, int rotary_dim, float rope_base,
-                          float softmax_scale, int dtype, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by both decode entry points (no device work).
+int validate_decode(const void* q, const void* k, const void* v, const void* k_cache,
+                    const void* v_cache, const int32_t* cache_lens, const void* o,
+                    const float* lse, int B, int H, int D, int cap, int rotary_dim,
+                    float rope_base, float softmax_scale, int dtype) {
   if (B < 1 || H < 1 || D < 1 || cap < 1) return NEOX_E_ARG;
   if ((int64_t)B * H * cap >= kMaxRows) return NEOX_E_ARG;
   if (dtype != NEOX_F32 && dtype != NEOX_BF16 && dtype != NEOX_F16) return NEOX_E_ARG;
@@ -436,14 +443,17 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   }
   if (o == q || o == k || o == v || o == k_cache || o == v_cache) return NEOX_E_ARG;
   if (D != 64 && D != 96 && D != 128) return NEOX_E_UNSUPPORTED;
-  const size_t need = neox_rope_attn_decode_workspace_size(B, H, D, cap);
-  if (!workspace || workspace_bytes < need) return NEOX_E_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NEOX_E_ALIGN;
+  return NEOX_OK;
+}
 
-  int dev = 0;
-  int st = check_device(&dev);
-  if (st != NEOX_OK) return st;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+// Enqueues one decoding step with chunk partials in `part` (validated
+// arguments; `dev` is the current device).  Without a scratch pointer
+// (part == nullptr) the per-device fixed array is used.
+int run_decode(int dev, const void* q, const void* k, const void* v, void* k_cache,
+               void* v_cache, const int32_t* cache_lens, void* o, float* lse, int B, int H,
+               int D, int cap, int rotary_dim, float rope_base, float softmax_scale, int dtype,
+               float* part, hipStream_t hs) {
+  int st = NEOX_OK;
   const float2* rope = nullptr;
   if (rotary_dim > 0 && (st = find_rope_table(dev, cap, rotary_dim, rope_base, &rope)) != NEOX_OK)
     return st;
@@ -466,8 +476,50 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
   p.v_cache = v_cache;
   p.o = o;
   p.lse = lse;
-  p.part = static_cast<float*>(workspace);
+  if (part == nullptr && p.nsplit > 1 && neox::decode_scratch(dev, &part) != hipSuccess) {
+    (void)hipGetLastError();
+    return NEOX_E_DEVICE;
+  }
+  p.part = part;
   return neox::launch_decode(p, hs) == hipSuccess ? NEOX_OK : NEOX_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, const int32_t* cache_lens, void* o, float* lse, int B,
+                          int H, int D, int cap, int rotary_dim, float rope_base,
+                          float softmax_scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = validate_decode(q, k, v, k_cache, v_cache, cache_lens, o, lse, B, H, D, cap,
+                           rotary_dim, rope_base, softmax_scale, dtype);
+  if (st != NEOX_OK) return st;
+  const size_t need = neox_rope_attn_decode_workspace_size(B, H, D, cap);
+  if (!workspace || workspace_bytes < need) return NEOX_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NEOX_E_ALIGN;
+  int dev = 0;
+  if ((st = check_device(&dev)) != NEOX_OK) return st;
+  return run_decode(dev, q, k, v, k_cache, v_cache, cache_lens, o, lse, B, H, D, cap,
+                    rotary_dim, rope_base, softmax_scale, dtype, static_cast<float*>(workspace),
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int neox_rope_attn_decode_noalloc(const void* q, const void* k, const void* v, void* k_cache,
+                                  void* v_cache, const int32_t* cache_lens, void* o, float* lse,
+                                  int B, int H, int D, int cap, int rotary_dim, float rope_base,
+                                  float softmax_scale, int dtype, void* stream) {
+  int st = validate_decode(q, k, v, k_cache, v_cache, cache_lens, o, lse, B, H, D, cap,
+                           rotary_dim, rope_base, softmax_scale, dtype);
+  if (st != NEOX_OK) return st;
+  if (neox_rope_attn_decode_workspace_size(B, H, D, cap) > NEOX_DECODE_SCRATCH_BYTES)
+    return NEOX_E_TOO_LARGE;
+  int dev = 0;
+  if ((st = check_device(&dev)) != NEOX_OK) return st;
+  return run_decode(dev, q, k, v, k_cache, v_cache, cache_lens, o, lse, B, H, D, cap,
+                    rotary_dim, rope_base, softmax_scale, dtype, nullptr,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int neox_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_scale,

@@ -74,6 +74,10 @@ extern "C" {
 #define NEOX_E_DEVICE (-6)      /* no usable gfx950 device / HIP runtime error */
 #define NEOX_E_ALLOC (-7)       /* rotary table allocation failed (neox_rope_table_prepare) */
 #define NEOX_E_NOT_PREPARED (-8) /* rotary table not prepared: call neox_rope_table_prepare */
+#define NEOX_E_TOO_LARGE (-9)   /* beyond NEOX_DECODE_SCRATCH_BYTES (no-allocation decode) */
+
+/* Size of the fixed device array behind neox_rope_attn_decode_noalloc. */
+#define NEOX_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
 
 /* Storage type of q, k, v, o, dout (and of dq, dk, dv unless out_dtype says fp32). */
 #define NEOX_F32 0
@@ -277,6 +281,28 @@ int neox_rope_attn_decode(const void* q, const void* k, const void* v, void* k_c
                           int B, int H, int D, int cap, int rotary_dim, float rope_base,
                           float softmax_scale, int dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * neox_rope_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step, the same kernels and the same results bit for
+ * bit, with no workspace argument.  The chunk partials go to a fixed
+ * NEOX_DECODE_SCRATCH_BYTES array that every device holds from the library's
+ * first use of it until the process ends.  The caller still passes every
+ * input and output (and prepares the rotary table, as for the other calls).
+ * Accepts the problems whose neox_rope_attn_decode_workspace_size() is at
+ * most NEOX_DECODE_SCRATCH_BYTES (for example B*H = 512 heads of D = 96 with
+ * an 8192-row cache); larger ones return NEOX_E_TOO_LARGE before any work.
+ * All calls on one device share its array: calls that may overlap on one
+ * device (different streams without ordering between them) race and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero:
+ * every partial a call reads is written earlier in the same call.  Other
+ * status codes as for neox_rope_attn_decode (never NEOX_E_WORKSPACE).
+ */
+int neox_rope_attn_decode_noalloc(const void* q, const void* k, const void* v, void* k_cache,
+                                  void* v_cache, const int32_t* cache_lens, void* o, float* lse,
+                                  int B, int H, int D, int cap, int rotary_dim, float rope_base,
+                                  float softmax_scale, int dtype, void* stream);
 
 /*
  * FP8 forward: causal (or full) attention with q~, k~ and v stored as FP8 E4M3

@@ -382,3 +382,23 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=300, cwd=root)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_noalloc_decode_validation(lib):
+    """The no-allocation decode checks its arguments like the workspace one and
+    refuses problems whose partials exceed its fixed array, before any device
+    work (so on a host without a GPU only a fitting call reaches E_DEV)."""
+    def call(B=2, H=4, D=64, cap=300, rd=16, q=A1, o=A7):
+        return lib.neox_rope_attn_decode_noalloc(q, A2, A3, A4, A5, A6, o, A8, B, H, D, cap, rd,
+                                                 1e4, 0.125, BF16, None)
+    assert call(q=None) == E_ARG
+    assert call(o=A1) == E_ARG
+    assert call(D=80) == E_UNSUP
+    big = (8, 64, 96, 16384)
+    assert lib.neox_rope_attn_decode_workspace_size(*big) > _lib.NEOX_DECODE_SCRATCH_BYTES
+    assert call(B=8, H=64, D=96, cap=16384) == -9
+    fits = (8, 64, 96, 8192)
+    assert lib.neox_rope_attn_decode_workspace_size(*fits) <= _lib.NEOX_DECODE_SCRATCH_BYTES
+    if not os.path.exists("/dev/kfd"):
+        assert call(B=8, H=64, D=96, cap=8192) == E_DEV
+    assert lib.neox_status_str(-9) != b"unknown status"
