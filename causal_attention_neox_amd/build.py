@@ -56,8 +56,25 @@ def _compile(hipcc: str, src: str, obj: str) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
+PROBE_SRC = os.path.join(CSRC, "probe", "mfma_clock.hip")
+PROBE_PATH = os.path.join(PKG_DIR, "libneoxprobe.so")
+
+
+def build_probe(hipcc: str) -> str:
+    """The measurement probe (MFMA rate and sustained clock) as its own small
+    library; it is no part of libneoxattn."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [hipcc, *COMMON_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build(jobs: int = 8) -> str:
-    """Compiles every source and links the shared library; returns its path."""
+    """Compiles every source and links the shared library (and the
+    measurement probe); returns the library's path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
@@ -70,6 +87,7 @@ def build(jobs: int = 8) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_probe(hipcc)
     return LIB_PATH
 
 
