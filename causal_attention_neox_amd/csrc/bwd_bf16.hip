@@ -46,10 +46,6 @@ __device__ __forceinline__ elem8 tr8(const uint16_t* p, int second) {
   const s16x4 a = tr4(p), b = tr4(p + second);
   return __builtin_bit_cast(elem8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_block) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
-                                   (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
-}
 
 // LDS tiles are rows of C 16-byte chunks, unpadded; chunk c of row r sits at
 // r*C + (c ^ swz(r)).  The swizzle keeps both access patterns conflict-free on
@@ -250,11 +246,11 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   // Fd[2 BMQ..); on the last tile rows past S re-read row S-1 (masked).
   auto fetch_q = [&](int qt, uint16_t* Qd, float* Fd) {
     const int q0 = qt * BMQ;
+    const buf_rsrc qr = raw_rsrc(qb + (int64_t)q0 * qstr);
+    const buf_rsrc gr = raw_rsrc(gb + (int64_t)q0 * p.sdo.s);
     if (q0 + BMQ <= S) {
-      const uint16_t* q_t = qb + (int64_t)q0 * qstr;
-      const uint16_t* g_t = gb + (int64_t)q0 * p.sdo.s;
 #pragma unroll
-      for (int n = 0; n < NFB; ++n) load_lds16((fdo[n] ? g_t : q_t) + foff[n], Qd + fdst[n]);
+      for (int n = 0; n < NFB; ++n) dma16(fdo[n] ? gr : qr, 2u * (uint32_t)foff[n], Qd + fdst[n]);
     } else {
 #pragma unroll
       for (int n = 0; n < NFB; ++n) {
@@ -262,15 +258,15 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int blk = fdo[n] ? fbk - CB : fbk;
         const int P = 64 * blk + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
-        const int rr = min(q0 + row, S - 1);
-        const uint16_t* src = fdo[n] ? gb + (int64_t)rr * p.sdo.s : qb + (int64_t)rr * qstr;
-        load_lds16(src + 8 * ch, Qd + fdst[n]);
+        const int rr = min(q0 + row, S - 1) - q0;
+        const int64_t str = fdo[n] ? p.sdo.s : qstr;
+        dma16(fdo[n] ? gr : qr, 2u * (uint32_t)(rr * str + 8 * ch), Qd + fdst[n]);
       }
     }
     if (wave < 2 && lane < BMQ / 4) {
       const float* src = wave == 0 ? nlb : dlb;
       if ((S & 3) == 0 && q0 + BMQ <= S) {  // 16-byte aligned, whole tile
-        load_lds16(src + q0 + 4 * lane, reinterpret_cast<uint16_t*>(Fd + wave * 2 * BMQ));
+        dma16(raw_rsrc(src + q0), 16u * (uint32_t)lane, Fd + wave * 2 * BMQ);
       } else {
         f32x4 w;
 #pragma unroll
@@ -285,14 +281,19 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // Stationary K~ (and V) tiles (2C blocks each, rows past S repeat row S-1)
   // and the first q-tile.
+  {
+    const buf_rsrc kr = raw_rsrc(kb + (int64_t)k0 * kstr);
+    const buf_rsrc vr = raw_rsrc(vb + (int64_t)k0 * p.sv.s);
 #pragma unroll
-  for (int n = 0; n < NKB; ++n) {
-    const int blk = wave + 8 * n;
-    const int P = 64 * blk + lane;
-    const int row = P / C, ch = (P % C) ^ swz<C>(row);
-    const int rr = min(k0 + row, S - 1);
-    load_lds16(kb + (int64_t)rr * kstr + 8 * ch, lds + L::KT + 512 * blk);
-    if constexpr (!kRegV) load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, lds + L::VT + 512 * blk);
+    for (int n = 0; n < NKB; ++n) {
+      const int blk = wave + 8 * n;
+      const int P = 64 * blk + lane;
+      const int row = P / C, ch = (P % C) ^ swz<C>(row);
+      const int rr = min(k0 + row, S - 1) - k0;
+      dma16(kr, 2u * (uint32_t)(rr * kstr + 8 * ch), lds + L::KT + 512 * blk);
+      if constexpr (!kRegV)
+        dma16(vr, 2u * (uint32_t)(rr * p.sv.s + 8 * ch), lds + L::VT + 512 * blk);
+    }
   }
   fetch_q(qt_lo, lds + L::Q0, fl);
   elem8 kreg[kRegK ? D / 16 : 1], vreg[kRegV ? D / 16 : 1];
@@ -701,22 +702,22 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
   }
   auto fetch = [&](int kt, uint16_t* Kd, uint16_t* Vd) {
     const int k0 = kt * DQ_BN;
+    const buf_rsrc kr = raw_rsrc(kb + (int64_t)k0 * kstr);
+    const buf_rsrc vr = raw_rsrc(vb + (int64_t)k0 * p.sv.s);
     if (k0 + DQ_BN <= S) {
-      const uint16_t* kt0 = kb + (int64_t)k0 * kstr;
-      const uint16_t* vt0 = vb + (int64_t)k0 * p.sv.s;
 #pragma unroll
       for (int n = 0; n < NTB; ++n) {
-        load_lds16(kt0 + koff[n], Kd + 512 * (wave + 4 * n));
-        load_lds16(vt0 + voff[n], Vd + 512 * (wave + 4 * n));
+        dma16(kr, 2u * (uint32_t)koff[n], Kd + 512 * (wave + 4 * n));
+        dma16(vr, 2u * (uint32_t)voff[n], Vd + 512 * (wave + 4 * n));
       }
     } else {
 #pragma unroll
       for (int n = 0; n < NTB; ++n) {
         const int P = 64 * (wave + 4 * n) + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
-        const int rr = min(k0 + row, S - 1);
-        load_lds16(kb + (int64_t)rr * kstr + 8 * ch, Kd + 512 * (wave + 4 * n));
-        load_lds16(vb + (int64_t)rr * p.sv.s + 8 * ch, Vd + 512 * (wave + 4 * n));
+        const int rr = min(k0 + row, S - 1) - k0;
+        dma16(kr, 2u * (uint32_t)(rr * kstr + 8 * ch), Kd + 512 * (wave + 4 * n));
+        dma16(vr, 2u * (uint32_t)(rr * p.sv.s + 8 * ch), Vd + 512 * (wave + 4 * n));
       }
     }
   };

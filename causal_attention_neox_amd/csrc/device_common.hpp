@@ -89,6 +89,25 @@ __device__ __forceinline__ elem8 lds_read8(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global -> LDS tile loads (16 bytes per lane) through a raw buffer
+// resource over a wave-uniform base, with a per-lane byte offset.  The
+// compiler's wait-count bookkeeping treats this buffer form as a vector-memory
+// load only, whereas it counts the global form against the LDS counter as
+// well; with a global-form tile load in flight every LDS operand wait then
+// becomes a full lgkmcnt(0), which leaves no LDS read in flight behind a
+// matrix product.  Word 3 of the resource selects 32-bit data (the gfx9 raw
+// buffer setting); offsets stay below 2^31 (bounded row strides, whole tiles).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+__device__ __forceinline__ void dma16(buf_rsrc r, uint32_t byte_off, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_block)), 16,
+      (int)byte_off, 0, 0, 0);
+}
+
 // Start and end (exclusive) of the document holding token t of one batch row.
 // off[0..n] lists document starts (off[0] = 0, off[n] = S, non-decreasing).
 // Results are clamped so that start <= t < end <= S even for malformed rows.

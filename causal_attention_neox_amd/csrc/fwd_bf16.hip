@@ -17,7 +17,7 @@
 //  * O^T += V^T P^T: B = P straight from the score registers; A = V^T read from
 //    the row-major V tile with ds_read_b64_tr_b16 (two 4-key reads per 8-key
 //    operand), so V needs no transposition anywhere.
-//  * K/V tiles go global -> LDS directly (global_load_lds_dwordx4) into an
+//  * K/V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds) into an
 //    unpadded, XOR-swizzled layout that keeps the operand reads free of bank
 //    conflicts; only the rotary dims of K pass through registers.  Two LDS
 //    buffers, one barrier per tile; every LDS operand address is a per-lane
@@ -54,11 +54,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
-}
-
-__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_block) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
-                                   (__attribute__((address_space(3))) void*)(lds_block), 16, 0, 0);
 }
 
 // LDS layout of a K or V tile: BN rows x D/8 chunks of 16 bytes, unpadded, chunk
@@ -146,17 +141,15 @@ struct TilePlan {
   __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, int64_t ks,
                                         const uint16_t* __restrict__ vb, int64_t vs, int k0,
                                         int S, int rd, uint16_t* Kt, uint16_t* Vt, int wave) {
+    // uniform tile base (buffer resource) + 32-bit per-lane byte offset
+    const buf_rsrc kr = raw_rsrc(kb + (int64_t)k0 * ks);
+    const buf_rsrc vr = raw_rsrc(vb + (int64_t)k0 * vs);
     if (k0 + BN <= S) {
-      const uint16_t* kt0 = kb + (int64_t)k0 * ks;
-      const uint16_t* vt0 = vb + (int64_t)k0 * vs;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int blk = wave + 4 * i;
-        // uniform tile base + 32-bit per-lane byte offset: the scalar-base
-        // addressing form, no 64-bit address arithmetic per load
-        load_lds16(reinterpret_cast<const char*>(vt0) + voff[i], Vt + 512 * blk);
-        if (kdirect & (1 << i))
-          load_lds16(reinterpret_cast<const char*>(kt0) + koff[i], Kt + 512 * blk);
+        dma16(vr, voff[i], Vt + 512 * blk);
+        if (kdirect & (1 << i)) dma16(kr, koff[i], Kt + 512 * blk);
       }
     } else {
       // last tile: rows past S re-read row S-1 (their keys are masked)
@@ -166,10 +159,10 @@ struct TilePlan {
         const int blk = wave + 4 * i;
         const int P = 64 * blk + lane;
         const int row = P / CPR;
-        const int r = min(k0 + row, S - 1);
-        load_lds16(vb + (int64_t)r * vs + 8 * ((P % CPR) ^ Swz<D>::v(row)), Vt + 512 * blk);
+        const int r = min(k0 + row, S - 1) - k0;
+        dma16(vr, 2u * (uint32_t)(r * vs + 8 * ((P % CPR) ^ Swz<D>::v(row))), Vt + 512 * blk);
         if (kdirect & (1 << i))
-          load_lds16(kb + (int64_t)r * ks + 8 * ((P % CPR) ^ Swz<D>::k(row)), Kt + 512 * blk);
+          dma16(kr, 2u * (uint32_t)(r * ks + 8 * ((P % CPR) ^ Swz<D>::k(row))), Kt + 512 * blk);
       }
     }
     const int half = rd >> 1;
@@ -483,11 +476,13 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
   uint16_t* qrows = lds + ((wave & 2) ? 3 * TILE : TILE) + (wave & 1) * 32 * D;
   if (ROT == 0 && !QROT) {
     const int r0 = q0 + wave * 32;
+    const int rb = min(r0, S - 1);  // rows past S re-read row S-1 (never stored)
+    const buf_rsrc qr = raw_rsrc(qb + (int64_t)rb * p.sq.s);
 #pragma unroll
     for (int i = 0; i < CPR / 2; ++i) {
       const int P = 64 * i + lane, row = P / CPR;
       const int ch = (P % CPR) ^ (row & QSW);
-      load_lds16(qb + (int64_t)min(r0 + row, S - 1) * p.sq.s + 8 * ch, qrows + 512 * i);
+      dma16(qr, 2u * (uint32_t)((min(r0 + row, S - 1) - rb) * p.sq.s + 8 * ch), qrows + 512 * i);
     }
   } else {
     const uint16_t* qrow = qb + (int64_t)qc * p.sq.s;

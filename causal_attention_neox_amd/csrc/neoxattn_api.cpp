@@ -139,12 +139,16 @@ int validate_common(const neox_attn_args* a) {
 }
 
 // Checks one tensor: pointer present and 16-byte aligned, strides non-negative
-// and multiples of the 16-byte unit (`unit` elements).
+// and multiples of the 16-byte unit (`unit` elements), row stride at most 2^22
+// elements.
 int check_tensor(const void* p, const neox_strides& s, int unit) {
   if (!p) return NEOX_E_ARG;
   if (s.batch < 0 || s.head < 0 || s.seq < 0) return NEOX_E_ARG;
   if (!aligned16(p)) return NEOX_E_ALIGN;
   if (s.batch % unit || s.head % unit || s.seq % unit) return NEOX_E_ALIGN;
+  // tile loads address up to 128 rows from a tile's first row with 32-bit
+  // byte offsets
+  if (s.seq > ((int64_t)1 << 22)) return NEOX_E_UNSUPPORTED;
   return NEOX_OK;
 }
 

@@ -41,7 +41,8 @@
  *  - Supported: D in {64, 96, 128}; 0 <= rotary_dim <= D, rotary_dim even;
  *    rope_base > 0 and finite; softmax_scale > 0 and finite; B, H, S >= 1;
  *    B*H*S < 2^31; tensor base pointers 16-byte aligned; row strides multiples
- *    of 8 elements (bf16, fp16) or 4 elements (fp32).
+ *    of 8 elements (bf16, fp16) or 4 elements (fp32), and at most 2^22
+ *    elements between consecutive rows (NEOX_E_UNSUPPORTED beyond).
  *  - The compute calls (forward, backward, decode, FP8 forward) allocate
  *    nothing and never wait: every buffer is the caller's, and the rotary
  *    cos/sin table of a (rotary_dim, rope_base) pair -- the per-layer

@@ -402,3 +402,15 @@ def test_noalloc_decode_validation(lib):
     if not os.path.exists("/dev/kfd"):
         assert call(B=8, H=64, D=96, cap=8192) == E_DEV
     assert lib.neox_status_str(-9) != b"unknown status"
+
+
+def test_ex_row_stride_bound(lib):
+    """Row strides beyond 2^22 elements are refused before any device work."""
+    strides = (_lib.NeoxStrides * 8)()
+    for n in range(8):
+        strides[n] = _lib.NeoxStrides(4 * 128 * 192, 128 * 192, 192)
+    strides[0] = _lib.NeoxStrides(0, 0, (1 << 22) + 8)
+    a = make_args(strides=ctypes.cast(strides, ctypes.POINTER(_lib.NeoxStrides)))
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) == E_UNSUP
+    strides[0] = _lib.NeoxStrides(0, 0, 1 << 22)
+    assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) in (OK, E_DEV)
