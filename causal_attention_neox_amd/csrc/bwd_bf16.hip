@@ -13,9 +13,10 @@
 //   dQ:    one workgroup per (batch, head, 128 queries), Q-stationary.  Its
 //          prologue forms the row terms Delta_i = dO_i . o_i and
 //          nlse_i = -lse_i log2(e) (with the ALiBi row term folded in) and
-//          writes them to the workspace; 64-key tiles stream through LDS, S and
-//          dP are recomputed, dQ~ += dS' K~ accumulates in registers, and the
-//          epilogue writes dq = scale R^T dQ~.
+//          writes them to the workspace (Delta negated: the dP accumulators
+//          start from -Delta, so dP - Delta costs no extra step); 64-key
+//          tiles stream through LDS, S and dP are recomputed, dQ~ += dS' K~
+//          accumulates in registers, and the epilogue writes dq = scale R^T dQ~.
 //   dK/dV: one workgroup per (batch, head, 128 keys), K-stationary; 64-row
 //          q-tiles (with their Delta and nlse) stream through LDS:
 //            S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     {
       constexpr bool kMasked = decltype(masked)::value;
       const int lo_off = qlo - qw0 - 4 * hh, hi_off = qhi - qw0 - 4 * hh;
-      // nlse of this lane's rows now; Delta is read during the last dP step.
+      // nlse of this lane's rows now; -Delta (stored negated) just before the
+      // dP products, which start from it.
       f32x4 n4[4], d4[4];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) n4[a4] = *reinterpret_cast<const f32x4*>(nlt + 8 * a4 + 4 * hh);
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int t = 0; t < NST; ++t) {
         if (t + PF < NST) ring[t + PF] = rd(t + PF);
-        if (t == 2 * NS - 2) {
+        if (t == NS - 2 || (NS < 2 && t == 0)) {
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4)
             d4[a4] = *reinterpret_cast<const f32x4*>(dlt + 8 * a4 + 4 * hh);
@@ -430,6 +432,14 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
           sacc = mfma32x32x16(o.a, kRegK ? kreg[kRegK ? t : 0] : o.b, sacc);
         } else if (t < 2 * NS) {
           const int c = t - NS;
+          if (c == 0) {
+            // dP starts from -Delta (register r: row 8 (r/4) + 4 hh + r%4),
+            // so the products leave dP - Delta
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dpacc[4 * a4 + e] = d4[a4][e];
+          }
           dpacc = mfma32x32x16(o.a, kRegV ? vreg[kRegV ? c : 0] : o.b, dpacc);
           // P for this step's share of register pairs
 #pragma unroll
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int r = 2 * pp + e;
-              x[e] = sacc[r] * (dpacc[r] - d4[r / 4][r % 4]);
+              x[e] = sacc[r] * dpacc[r];
             }
             sw[pp / 4][pp % 4] = pack2(x[0], x[1]);
           }
@@ -751,11 +761,15 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
   float nl = -lse_i * kLog2e;
   if (a.alibi) nl -= alibi_slope_log2(a, h) * (float)qc;
   if (qi < S && hh == 0) {
-    p.delta[(int64_t)bh * S + qi] = dsum;
+    p.delta[(int64_t)bh * S + qi] = -dsum;  // stored negated: the dK/dV pass starts dP there
     p.nlse[(int64_t)bh * S + qi] = nl;
   }
   if (qi >= S) nl = 0.0f;
   const float dl = qi < S ? dsum : 0.0f;
+  constexpr bool kNdl = D == 96;  // D = 64 would lose its third wave per SIMD to the 16 registers
+  f32x16 ndl16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl16[r] = kNdl ? -dl : 0.0f;
   const float c2 = a.scale_log2;
   const float sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
 
@@ -793,7 +807,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
     // The tile's two 32-key halves one after the other (bounds the registers).
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // dP accumulates from -Delta_i where the registers allow a constant block
+      f32x16 sacc = f32x16{}, dpacc = kNdl ? ndl16 : f32x16{};
       // K~ / V rows of dims step c, read one step ahead of their MFMAs.
       auto rows = [&](int c, elem8& kr, elem8& vr) {
         const int off = 8 * (ql * C + ((2 * c + hh) ^ rsw)) + 32 * blk * D;
@@ -823,7 +838,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
           const float bias = ALIBI ? kbase + sl2 * (float)ko : nl;
           float pr = fast_exp2(__builtin_fmaf(sacc[r], c2, bias));
           if (kMasked && (ko < jlo || ko > jhi)) pr = 0.0f;
-          dpacc[r] = pr * (dpacc[r] - dl);
+          dpacc[r] = pr * (kNdl ? dpacc[r] : dpacc[r] - dl);
         }
       };
       if (masked) {
