@@ -3,16 +3,18 @@
 // The bf16 MFMA path cannot meet an fp32 accuracy bound, so fp32 inputs run on
 // the vector ALUs: the same tiled, online-softmax algorithm (exact attention,
 // "GPT-NeoX 开源训练框架深度解读", section "问题二：注意力计算太慢") with K/V
-// tiles of 32 keys staged in LDS.  Two lanes share a query row, each holding
-// half of the head dims; the two partial dot products meet with one lane swap.
+// tiles of 32 keys staged in LDS.  Eight lanes share a query row, each
+// holding an eighth of the head dims; the partial dot products meet with three
+// lane swaps.
 #include "device_common.hpp"
 
 namespace neox {
 namespace {
 
-constexpr int QB = 64;          // queries per workgroup
+constexpr int QB = 16;          // queries per workgroup
+constexpr int LQ = 8;           // lanes per query, each with D / 8 dims
 constexpr int KB = 32;          // keys per tile
-constexpr int NT = 2 * QB;      // two lanes per query
+constexpr int NT = QB * LQ;     // 128 threads
 
 // Rotated value of dim d of an fp32 row at position pos (rotate-half pairs).
 __device__ __forceinline__ float rot_elem_f32(const float* row, int d, int pos, int rd,
@@ -28,11 +30,20 @@ __device__ __forceinline__ float rot_elem_f32(const float* row, int d, int pos, 
   return x * cs.x + row[d - half] * cs.y;
 }
 
+// Small problems are latency bound (one fp32 S=128 head pair is a handful of
+// workgroups), so every global load of a tile -- K and V rows and the rotary
+// table entries of its keys -- is issued at once into registers, one tile
+// ahead of the tile being computed; the raw rows then go to LDS and the rotary
+// pairs of K are turned in place there.
 template <int D>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
-  constexpr int DH = D / 2;
-  __shared__ float Ks[KB][D + 1];
-  __shared__ float Vs[KB][D + 1];
+  constexpr int DL = D / LQ;                 // dims per lane
+  constexpr int RS = D + 4;                  // LDS row stride (floats), 16-byte rows
+  constexpr int NV4 = KB * D / 4 / NT;       // float4 of K (and of V) per thread per tile
+  constexpr int NCS = KB * (D / 2) / NT;     // rotary pairs per thread per tile, at most
+  static_assert(DL % 4 == 0 && (KB * D / 4) % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) float Ks[KB * RS];
+  __shared__ __attribute__((aligned(16))) float Vs[KB * RS];
 
   const AttnShape& a = p.a;
   const int S = a.S;
@@ -42,10 +53,11 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int half_id = tid & 1;
+  const int part = tid & (LQ - 1);
   const int q0 = qt * QB;
-  const int qi = q0 + (tid >> 1);
+  const int qi = q0 + tid / LQ;
   const int qc = qi < S ? qi : S - 1;
+  const int rd = a.rd, half = rd >> 1;
 
   const float* qb = (const float*)p.q + b * p.sq.b + h * p.sq.h;
   const float* kb = (const float*)p.k + b * p.sk.b + h * p.sk.h;
@@ -71,42 +83,81 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   }
   if (a.causal && qlast < bhi) bhi = qlast;
 
-  float qh[DH], oh[DH];
-  {
-    const float* qrow = qb + (int64_t)qc * p.sq.s;
+  // Tile prefetch registers: raw K and V rows, rotary (cos, sin) of the pairs.
+  f32x4 kr[NV4], vr[NV4];
+  float2 cs[NCS > 0 ? NCS : 1];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int e = 0; e < DH; ++e) {
-      const int d = half_id * DH + e;
-      qh[e] = qi < S ? rot_elem_f32(qrow, d, qi, a.rd, a.rope) : 0.0f;
-      oh[e] = 0.0f;
+    for (int i = 0; i < NV4; ++i) {
+      const int idx = tid + NT * i, row = idx / (D / 4), c4 = idx % (D / 4);
+      const int j = min(k0 + row, S - 1);
+      kr[i] = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * p.sk.s + 4 * c4);
+      vr[i] = *reinterpret_cast<const f32x4*>(vb + (int64_t)j * p.sv.s + 4 * c4);
     }
+#pragma unroll
+    for (int i = 0; i < NCS; ++i) {
+      const int it = tid + NT * i;
+      if (it < KB * half) {
+        const int row = it / half, d = it % half;
+        cs[i] = a.rope[(int64_t)min(k0 + row, S - 1) * half + d];
+      }
+    }
+  };
+
+  float qh[DL], oh[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) {
+    qh[e] = qi < S ? rot_elem_f32(qb + (int64_t)qc * p.sq.s, part * DL + e, qi, rd, a.rope) : 0.0f;
+    oh[e] = 0.0f;
   }
   const float slope = a.alibi ? (a.slopes ? a.slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)a.H))
                               : 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int k0 = (blo / KB) * KB; k0 <= bhi; k0 += KB) {
-    __syncthreads();
-    for (int it = tid; it < KB * D; it += NT) {
-      const int r = it / D, d = it % D;
-      const int j = k0 + r;
-      float kv = 0.0f, vv = 0.0f;
-      if (j < S) {
-        kv = rot_elem_f32(kb + (int64_t)j * p.sk.s, d, j, a.rd, a.rope);
-        vv = vb[(int64_t)j * p.sv.s + d];
+  const int kfirst = (blo / KB) * KB;
+  if (kfirst <= bhi) fetch(kfirst);
+  for (int k0 = kfirst; k0 <= bhi; k0 += KB) {
+    __syncthreads();  // the previous tile is no longer read
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int idx = tid + NT * i, row = idx / (D / 4), c4 = idx % (D / 4);
+      *reinterpret_cast<f32x4*>(Ks + row * RS + 4 * c4) = kr[i];
+      *reinterpret_cast<f32x4*>(Vs + row * RS + 4 * c4) = vr[i];
+    }
+    if (rd > 0) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NCS; ++i) {
+        const int it = tid + NT * i;
+        if (it < KB * half) {
+          const int row = it / half, d = it % half;
+          const float x1 = Ks[row * RS + d], x2 = Ks[row * RS + d + half];
+          Ks[row * RS + d] = x1 * cs[i].x - x2 * cs[i].y;
+          Ks[row * RS + d + half] = x2 * cs[i].x + x1 * cs[i].y;
+        }
       }
-      Ks[r][d] = kv;
-      Vs[r][d] = vv;
     }
     __syncthreads();
+    if (k0 + KB <= bhi) fetch(k0 + KB);  // next tile's loads fly during this one
+
     float sc[KB];
     float mloc = -INFINITY;
-#pragma unroll 4
-    for (int r = 0; r < KB; ++r) {
-      float part = 0.0f;
 #pragma unroll
-      for (int e = 0; e < DH; ++e) part = fmaf(qh[e], Ks[r][half_id * DH + e], part);
-      float s = (part + __shfl_xor(part, 1)) * a.scale;
+    for (int r = 0; r < KB; ++r) {
+      const float* krow = Ks + r * RS + part * DL;
+      float acc = 0.0f;
+#pragma unroll
+      for (int e4 = 0; e4 < DL / 4; ++e4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + 4 * e4);
+        acc = fmaf(qh[4 * e4], kv[0], acc);
+        acc = fmaf(qh[4 * e4 + 1], kv[1], acc);
+        acc = fmaf(qh[4 * e4 + 2], kv[2], acc);
+        acc = fmaf(qh[4 * e4 + 3], kv[3], acc);
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      float s = acc * a.scale;
       const int j = k0 + r;
       if (a.alibi) s -= slope * (float)(qi - j);
       if (j < lo || j > hi) s = -INFINITY;
@@ -118,23 +169,33 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     const float alpha = expf(m_run - m_use);
     l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < DH; ++e) oh[e] *= alpha;
-#pragma unroll 4
+    for (int e = 0; e < DL; ++e) oh[e] *= alpha;
+#pragma unroll
     for (int r = 0; r < KB; ++r) {
       const float pr = expf(sc[r] - m_use);
       l_run += pr;
+      const float* vrow = Vs + r * RS + part * DL;
 #pragma unroll
-      for (int e = 0; e < DH; ++e) oh[e] = fmaf(pr, Vs[r][half_id * DH + e], oh[e]);
+      for (int e4 = 0; e4 < DL / 4; ++e4) {
+        const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + 4 * e4);
+        oh[4 * e4] = fmaf(pr, vv[0], oh[4 * e4]);
+        oh[4 * e4 + 1] = fmaf(pr, vv[1], oh[4 * e4 + 1]);
+        oh[4 * e4 + 2] = fmaf(pr, vv[2], oh[4 * e4 + 2]);
+        oh[4 * e4 + 3] = fmaf(pr, vv[3], oh[4 * e4 + 3]);
+      }
     }
     m_run = m_new;
   }
 
   if (qi < S) {
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    if (half_id == 0) p.lse[(int64_t)bh * S + qi] = m_run + logf(l_run);
-    float* orow = (float*)p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s + half_id * DH;
+    if (part == 0) p.lse[(int64_t)bh * S + qi] = m_run + logf(l_run);
+    float* orow = (float*)p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s + part * DL;
 #pragma unroll
-    for (int e = 0; e < DH; ++e) orow[e] = oh[e] * inv_l;
+    for (int e4 = 0; e4 < DL / 4; ++e4)
+      *reinterpret_cast<f32x4*>(orow + 4 * e4) =
+          f32x4{oh[4 * e4] * inv_l, oh[4 * e4 + 1] * inv_l, oh[4 * e4 + 2] * inv_l,
+                oh[4 * e4 + 3] * inv_l};
   }
 }
 
