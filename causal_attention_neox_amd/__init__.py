@@ -30,7 +30,7 @@ __all__ = [
     "neox_attn_fwd_ex", "neox_attn_bwd_ex",
     "neox_rope_attn_decode_workspace_size", "neox_rope_attn_decode",
     "neox_rope_attn_decode_noalloc", "neox_attn_fwd_fp8",
-    "neox_check_doc_offsets", "neox_rope_table_prepare", "attention",
+    "neox_check_doc_offsets", "neox_rope_table_prepare", "neox_attn_plan", "attention",
     "NEOX_F32", "NEOX_BF16", "NEOX_F16", "NEOX_POS_NONE", "NEOX_POS_ROPE", "NEOX_POS_ALIBI",
     "NEOX_OUT_SAME", "NEOX_OUT_F32",
 ]
@@ -275,6 +275,22 @@ def neox_check_doc_offsets(offsets_host, S: int) -> int:
     B, n1 = arr.shape
     return int(_lib.load().neox_check_doc_offsets(arr.ctypes.data_as(ctypes.c_void_p), B,
                                                   n1 - 1, int(S)))
+
+
+def neox_attn_plan(q, *, pos: int = NEOX_POS_ROPE, rotary_dim: int = 0, alibi_slopes=None,
+                   doc_offsets=None, causal: bool = True, fwd_workspace: bool = True,
+                   reuse_rotated_qk: bool = False) -> dict:
+    """Calls neox_attn_plan for a call on tensors shaped and typed like q: the
+    kernel forms the forward and the backward would launch (no device work)."""
+    a, keep = _make_args(q, pos=pos, rotary_dim=rotary_dim, rope_base=10000.0,
+                         alibi_slopes=alibi_slopes, causal=causal, softmax_scale=None,
+                         doc_offsets=doc_offsets, out_f32=False, tensors=[None] * 8,
+                         reuse_rotated_qk=reuse_rotated_qk)
+    plan = _lib.NeoxPlan()
+    st = _lib.load().neox_attn_plan(ctypes.byref(a), int(bool(fwd_workspace)), ctypes.byref(plan))
+    del keep
+    _check(st, "neox_attn_plan")
+    return {name: int(getattr(plan, name)) for name, _ in _lib.NeoxPlan._fields_}
 
 
 def neox_rope_table_prepare(max_S: int, rotary_dim: int, rope_base: float = 10000.0) -> None:

@@ -53,6 +53,11 @@ class NeoxAttnArgs(ctypes.Structure):
     ]
 
 
+class NeoxPlan(ctypes.Structure):
+    _fields_ = [("fp32_path", c_int), ("fwd_rotation_pass", c_int), ("fwd_k_staging", c_int),
+                ("fwd_rotate_q", c_int), ("alibi", c_int), ("bwd_rotation_pass", c_int)]
+
+
 SIGNATURES = {
     "neox_status_str": (ctypes.c_char_p, [c_int]),
     "neox_rope_attn_fwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
@@ -83,6 +88,7 @@ SIGNATURES = {
                                   c_float, c_int, c_void_p]),
     "neox_check_doc_offsets": (c_int, [c_void_p, c_int, c_int, c_int]),
     "neox_rope_table_prepare": (c_int, [c_int, c_int, c_float]),
+    "neox_attn_plan": (c_int, [ctypes.POINTER(NeoxAttnArgs), c_int, ctypes.POINTER(NeoxPlan)]),
 }
 
 _lock = threading.Lock()

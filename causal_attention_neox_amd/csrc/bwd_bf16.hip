@@ -973,7 +973,8 @@ template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
   if ((e = record_event(ev, 0, st)) != hipSuccess) return e;
-  if (p.a.rd > 0 && !p.qk_ready) {
+  const BwdPlan plan = bwd_plan16(p.a.rd, p.a.alibi != 0, p.qk_ready != 0);
+  if (plan.rotation_pass) {
     hipLaunchKernelGGL((bwd_prep_kernel<D>), row_grid<D>(p), dim3(256), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -981,14 +982,14 @@ hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   // dQ first: it also writes Delta and nlse, which the dK/dV pass reads.
   const unsigned BH = (unsigned)(p.a.B * p.a.H);
   const dim3 qgrid((unsigned)((p.a.S + DQ_BM - 1) / DQ_BM) * BH);
-  if (p.a.alibi)
+  if (plan.alibi)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(NT), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
   const dim3 kgrid((unsigned)((p.a.S + BNK - 1) / BNK) * BH);
-  if (p.a.alibi)
+  if (plan.alibi)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(NT8), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(NT8), 0, st, p);

@@ -674,12 +674,12 @@ hipError_t launch_d(const FwdParams& p, hipStream_t st) {
 template <int D>
 hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) {
   hipError_t e;
-  const int rd = p.a.rd;
-  if (p.a.alibi) {  // ALiBi runs without rotary
+  const FwdPlan plan = fwd_plan16(p.a.rd, p.a.alibi != 0, p.qrot != nullptr);
+  if (plan.alibi) {  // ALiBi runs without rotary
     if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
     return launch_d<D, 0, true, false>(p, st);
   }
-  if (rd > 0 && p.qrot) {
+  if (plan.rotation_pass) {
     // one wave per (position, group of kRopeNR * RPW heads), four waves per block
     const int64_t hpw = kRopeNR * RowGroups<D>::RPW;
     const int64_t waves = (p.a.B * p.a.H + hpw - 1) / hpw * p.a.S;
@@ -696,10 +696,12 @@ hipError_t launch_dim(const FwdParams& p, hipStream_t st, const hipEvent_t* ev) 
     return launch_d<D, 0, false, false>(q, st);
   }
   if ((e = record_event(ev, 1, st)) != hipSuccess) return e;
-  if (rd == 0) return launch_d<D, 0, false, false>(p, st);
-  if (rd % 16 == 0) return launch_d<D, 1, false, true>(p, st);
-  if (rd % 8 == 0) return launch_d<D, 2, false, true>(p, st);
-  return launch_d<D, 3, false, true>(p, st);
+  switch (plan.rot_mode) {
+    case 1: return launch_d<D, 1, false, true>(p, st);
+    case 2: return launch_d<D, 2, false, true>(p, st);
+    case 3: return launch_d<D, 3, false, true>(p, st);
+    default: return launch_d<D, 0, false, false>(p, st);
+  }
 }
 
 }  // namespace

@@ -106,6 +106,35 @@ hipError_t decode_scratch(int dev, float** out);
 
 hipError_t launch_rope_table(float2* table, int S, int rd, double base, hipStream_t st);
 
+// Which kernel forms a 16-bit call launches: decided here, on the host, and
+// used both by the launchers and by neox_attn_plan.
+struct FwdPlan {
+  int rotation_pass;  // q~, k~ row pass into the workspace, then the rotation-free kernel
+  int rot_mode;       // K staging of the attention kernel: 0 plain or pre-rotated, 1 rotary
+                      // pairs 8 wide (rd % 16 == 0), 2 pairs 4 wide (rd % 8 == 0), 3 every
+                      // chunk through registers
+  int rotate_q;       // the attention kernel rotates Q~ as it loads it
+  int alibi;
+};
+inline FwdPlan fwd_plan16(int rd, bool alibi, bool workspace) {
+  FwdPlan f{0, 0, 0, alibi ? 1 : 0};
+  if (alibi || rd == 0) return f;
+  if (workspace) {
+    f.rotation_pass = 1;
+    return f;
+  }
+  f.rotate_q = 1;
+  f.rot_mode = rd % 16 == 0 ? 1 : (rd % 8 == 0 ? 2 : 3);
+  return f;
+}
+struct BwdPlan {
+  int rotation_pass;  // the backward rotates q and k into the workspace itself
+  int alibi;
+};
+inline BwdPlan bwd_plan16(int rd, bool alibi, bool qk_ready) {
+  return BwdPlan{(rd > 0 && !qk_ready) ? 1 : 0, alibi ? 1 : 0};
+}
+
 // `ev` is null or 3 events: [0] is recorded by the caller before the call;
 // the launcher records [1] after the q/k rotation pass (before the attention
 // kernel when there is none); the caller records [2] after the call.

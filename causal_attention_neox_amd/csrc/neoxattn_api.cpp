@@ -109,6 +109,12 @@ int build_rope_table(int dev, int S, int rd, float base, const float2** out) {
 
 // ---------------------------------------------------------------- validation
 
+// The backward may take q~, k~ from a workspace the forward left them in.
+bool qk_ready(const neox_attn_args* a) {
+  return a->reuse_rotated_qk && a->dtype != NEOX_F32 && a->pos == NEOX_POS_ROPE &&
+         a->rotary_dim > 0;
+}
+
 int validate_common(const neox_attn_args* a) {
   if (!a) return NEOX_E_ARG;
   if (a->B < 1 || a->H < 1 || a->S < 1 || a->D < 1) return NEOX_E_ARG;
@@ -373,8 +379,7 @@ int neox_attn_bwd_ex(const neox_attn_args* a, const void* q, const void* k, cons
   p.sdq = to_internal(s ? s[5] : def);
   p.sdk = to_internal(s ? s[6] : def);
   p.sdv = to_internal(s ? s[7] : def);
-  p.qk_ready = (a->reuse_rotated_qk && a->dtype != NEOX_F32 && a->pos == NEOX_POS_ROPE &&
-                a->rotary_dim > 0) ? 1 : 0;
+  p.qk_ready = qk_ready(a) ? 1 : 0;
   p.out_f32 = (a->dtype == NEOX_F32 || a->out_dtype == NEOX_OUT_F32) ? 1 : 0;
   const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(a->phase_events);
   const hipError_t e = a->dtype == NEOX_BF16  ? neox::launch_bwd_bf16(p, hs, ev)
@@ -571,6 +576,28 @@ int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S
     for (int d = 0; d < n_docs; ++d)
       if (row[d + 1] < row[d]) return NEOX_E_ARG;
   }
+  return NEOX_OK;
+}
+
+int neox_attn_plan(const neox_attn_args* a, int fwd_workspace, neox_plan* out) {
+  if (!out) return NEOX_E_ARG;
+  const int st = validate_common(a);
+  if (st != NEOX_OK) return st;
+  if (fwd_workspace != 0 && fwd_workspace != 1) return NEOX_E_ARG;
+  *out = neox_plan{};
+  out->fp32_path = a->dtype == NEOX_F32;
+  if (out->fp32_path) {
+    out->alibi = a->pos == NEOX_POS_ALIBI;
+    return NEOX_OK;
+  }
+  const int rd = a->pos == NEOX_POS_ROPE ? a->rotary_dim : 0;
+  const neox::FwdPlan f = neox::fwd_plan16(rd, a->pos == NEOX_POS_ALIBI, fwd_workspace != 0);
+  const neox::BwdPlan b = neox::bwd_plan16(rd, a->pos == NEOX_POS_ALIBI, qk_ready(a));
+  out->fwd_rotation_pass = f.rotation_pass;
+  out->fwd_k_staging = f.rot_mode;
+  out->fwd_rotate_q = f.rotate_q;
+  out->alibi = f.alibi;
+  out->bwd_rotation_pass = b.rotation_pass;
   return NEOX_OK;
 }
 

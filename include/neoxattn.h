@@ -336,6 +336,33 @@ int neox_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_sc
  */
 int neox_check_doc_offsets(const int32_t* host_offsets, int B, int n_docs, int S);
 
+/* Kernel forms a call with given arguments runs (see neox_attn_plan). */
+typedef struct neox_plan {
+  int fp32_path;          /* fp32 storage: the vector-ALU kernels (no other field applies) */
+  int fwd_rotation_pass;  /* forward: a row pass writes q~ = R q, k~ = R k to the workspace,
+                             then the rotation-free attention kernel runs */
+  int fwd_k_staging;      /* forward attention kernel's K tiles: 0 plain or pre-rotated,
+                             1 rotary pairs 8 wide (rotary_dim % 16 == 0), 2 pairs 4 wide
+                             (rotary_dim % 8 == 0), 3 every chunk through registers */
+  int fwd_rotate_q;       /* forward attention kernel rotates Q~ as it loads it */
+  int alibi;              /* the ALiBi forms of the kernels */
+  int bwd_rotation_pass;  /* backward: rotates q and k into its workspace itself (no
+                             rotated rows reused from the forward) */
+} neox_plan;
+
+/*
+ * Which kernel forms the forward (with fwd_workspace = 1: a workspace given)
+ * and the backward (its reuse_rotated_qk taken from *a) would launch for these
+ * arguments -- the same host-side choice the launchers make -- without
+ * touching any device.  The forms follow the rotation's place in the pages'
+ * method (q and k rotated before attention, "FasterTransformer GPT-NeoX
+ * 推理指南", the rotary_embedding field of the 20B configuration) and the
+ * ALiBi alternative ("GPT-NeoX 开源训练框架深度解读", section "架构创新").
+ * Returns NEOX_OK, NEOX_E_ARG (as for neox_attn_fwd_ex's arguments, NULL out)
+ * or NEOX_E_UNSUPPORTED.
+ */
+int neox_attn_plan(const neox_attn_args* a, int fwd_workspace, neox_plan* out);
+
 /*
  * Set-up call: builds the rotary cos/sin table of the current device for
  * positions 0..max_S-1, rotary_dim and rope_base (the checkpoint's

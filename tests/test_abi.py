@@ -414,3 +414,51 @@ def test_ex_row_stride_bound(lib):
     assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) == E_UNSUP
     strides[0] = _lib.NeoxStrides(0, 0, 1 << 22)
     assert lib.neox_attn_fwd_ex(ctypes.byref(a), A1, A2, A3, A4, A5, None, 0, None) in (OK, E_DEV)
+
+
+def plan(lib, **kw):
+    ws = kw.pop("ws", 1)
+    a = make_args(**kw)
+    out = _lib.NeoxPlan()
+    st = lib.neox_attn_plan(ctypes.byref(a), ws, ctypes.byref(out))
+    return st, {n: getattr(out, n) for n, _ in _lib.NeoxPlan._fields_}
+
+
+@pytest.mark.parametrize("kw,expect", [
+    # with a forward workspace: the row pass, then the rotation-free kernel
+    (dict(D=96, rotary_dim=24), dict(fwd_rotation_pass=1, fwd_k_staging=0, fwd_rotate_q=0)),
+    (dict(D=128, rotary_dim=128), dict(fwd_rotation_pass=1, fwd_k_staging=0, fwd_rotate_q=0)),
+    # without one: the kernel rotates Q~ and stages K by the rotary width
+    (dict(D=128, rotary_dim=128, ws=0), dict(fwd_rotation_pass=0, fwd_k_staging=1, fwd_rotate_q=1)),
+    (dict(D=64, rotary_dim=16, ws=0), dict(fwd_k_staging=1, fwd_rotate_q=1)),
+    (dict(D=96, rotary_dim=24, ws=0), dict(fwd_k_staging=2, fwd_rotate_q=1)),
+    (dict(D=128, rotary_dim=40, ws=0), dict(fwd_k_staging=2, fwd_rotate_q=1)),
+    (dict(D=96, rotary_dim=6, ws=0), dict(fwd_k_staging=3, fwd_rotate_q=1)),
+    (dict(D=64, rotary_dim=2, ws=0), dict(fwd_k_staging=3, fwd_rotate_q=1)),
+    # no rotation, ALiBi, fp32
+    (dict(rotary_dim=0), dict(fwd_rotation_pass=0, fwd_k_staging=0, fwd_rotate_q=0,
+                              bwd_rotation_pass=0)),
+    (dict(rotary_dim=0, ws=0), dict(fwd_rotation_pass=0, fwd_k_staging=0, fwd_rotate_q=0)),
+    (dict(pos=2, rotary_dim=0), dict(alibi=1, fwd_rotation_pass=0, fwd_k_staging=0,
+                                     bwd_rotation_pass=0)),
+    (dict(dtype=F32, rotary_dim=16), dict(fp32_path=1, fwd_rotation_pass=0, fwd_rotate_q=0)),
+    (dict(dtype=2, rotary_dim=24, D=96, ws=0), dict(fp32_path=0, fwd_k_staging=2)),
+    # backward: rotates q, k itself unless the forward's rotated rows are reused
+    (dict(rotary_dim=16), dict(bwd_rotation_pass=1)),
+    (dict(rotary_dim=16, reuse_rotated_qk=1), dict(bwd_rotation_pass=0)),
+])
+def test_kernel_plan(lib, kw, expect):
+    """The host-side choice of kernel forms (shared by the launchers)."""
+    st, got = plan(lib, **kw)
+    assert st == OK
+    for k, v in expect.items():
+        assert got[k] == v, (k, got)
+
+
+def test_kernel_plan_validation(lib):
+    assert plan(lib, D=80)[0] == E_UNSUP
+    assert plan(lib, rotary_dim=15)[0] == E_ARG
+    assert plan(lib, ws=2)[0] == E_ARG
+    assert lib.neox_attn_plan(None, 1, None) == E_ARG
+    a = make_args()
+    assert lib.neox_attn_plan(ctypes.byref(a), 1, None) == E_ARG
