@@ -369,8 +369,9 @@ def workload_legs(args, torch, np, neox, W):
 def small_s_sweep(args, torch, np, neox, W):
     """The forward at S = 128, 256, 512 with the B*H and D of the S=2048, D=128
     shape (B=4, H=32, full rotary, bf16): few pairs per byte, so reported as the
-    HBM rate of the algorithmic bytes (one fused kernel, rotation in the tile
-    loads: no workspace)."""
+    HBM rate of the algorithmic bytes, for the call with a workspace (rotation
+    pass, then the rotation-free kernel: the faster form) and without one (the
+    kernel rotates q and k as it loads them)."""
     base = W.WORKLOADS[W.FWD_TARGET_WORKLOAD]
     out = []
     for S in (128, 256, 512):
@@ -380,16 +381,23 @@ def small_s_sweep(args, torch, np, neox, W):
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
         neox.neox_rope_table_prepare(S, wl.rotary_dim, wl.rope_base)
-        fwd = lambda: neox.neox_attn_fwd_ex(  # noqa: E731
-            q, k, v, o, lse, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base,
-            softmax_scale=wl.softmax_scale)
-        med, mean = per_call_ms(torch, fwd, max(4 * args.steps, 100), args.warmup)
+        fws = torch.empty(neox.neox_rope_attn_fwd_workspace_size(wl.B, wl.H, S, wl.D),
+                          dtype=torch.uint8, device="cuda")
+        t = {}
+        for tag, w in (("ws", fws), ("no_ws", None)):
+            fwd = lambda w=w: neox.neox_attn_fwd_ex(  # noqa: E731
+                q, k, v, o, lse, rotary_dim=wl.rotary_dim, rope_base=wl.rope_base,
+                softmax_scale=wl.softmax_scale, workspace=w)
+            t[tag] = per_call_ms(torch, fwd, max(4 * args.steps, 100), args.warmup)
+        med, mean = t["ws"]
         nb = fwd_bytes(wl)
         gbs = nb / (med * 1e-3) / 1e9
         out.append({"B": wl.B, "H": wl.H, "S": S, "D": wl.D, "us": round(med * 1e3, 2),
                     "us_mean": round(mean * 1e3, 2), "bytes": nb, "gbs": round(gbs, 1),
                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                    "tflops": round(4 * wl.D * W.total_pairs(inp) / (med * 1e-3) / 1e12, 2)})
+                    "tflops": round(4 * wl.D * W.total_pairs(inp) / (med * 1e-3) / 1e12, 2),
+                    "us_no_workspace": round(t["no_ws"][0] * 1e3, 2),
+                    "gbs_no_workspace": round(nb / (t["no_ws"][0] * 1e-3) / 1e9, 1)})
     return out
 
 
