@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int P = 64 * blk + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
         const int rr = min(q0 + row, S - 1) - q0;
-        const int64_t str = fdo[n] ? p.sdo.s : qstr;
+        const int str = (int)(fdo[n] ? p.sdo.s : qstr);  // offsets stay 32-bit (bounded strides)
         dma16(fdo[n] ? gr : qr, 2u * (uint32_t)(rr * str + 8 * ch), Qd + fdst[n]);
       }
     }
@@ -291,9 +291,9 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int P = 64 * blk + lane;
       const int row = P / C, ch = (P % C) ^ swz<C>(row);
       const int rr = min(k0 + row, S - 1) - k0;
-      dma16(kr, 2u * (uint32_t)(rr * kstr + 8 * ch), lds + L::KT + 512 * blk);
+      dma16(kr, 2u * (uint32_t)(rr * (int)kstr + 8 * ch), lds + L::KT + 512 * blk);
       if constexpr (!kRegV)
-        dma16(vr, 2u * (uint32_t)(rr * p.sv.s + 8 * ch), lds + L::VT + 512 * blk);
+        dma16(vr, 2u * (uint32_t)(rr * (int)p.sv.s + 8 * ch), lds + L::VT + 512 * blk);
     }
   }
   fetch_q(qt_lo, lds + L::Q0, fl);
@@ -726,8 +726,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
         const int P = 64 * (wave + 4 * n) + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
         const int rr = min(k0 + row, S - 1) - k0;
-        dma16(kr, 2u * (uint32_t)(rr * kstr + 8 * ch), Kd + 512 * (wave + 4 * n));
-        dma16(vr, 2u * (uint32_t)(rr * p.sv.s + 8 * ch), Vd + 512 * (wave + 4 * n));
+        dma16(kr, 2u * (uint32_t)(rr * (int)kstr + 8 * ch), Kd + 512 * (wave + 4 * n));
+        dma16(vr, 2u * (uint32_t)(rr * (int)p.sv.s + 8 * ch), Vd + 512 * (wave + 4 * n));
       }
     }
   };
@@ -835,7 +835,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ko = 8 * (r >> 2) + (r & 3);
-          const float bias = ALIBI ? kbase + sl2 * (float)ko : nl;
+          const float bias = ALIBI ? __builtin_fmaf(sl2, (float)ko, kbase) : nl;  // fma: not hoisted as 16 products
           float pr = fast_exp2(__builtin_fmaf(sacc[r], c2, bias));
           if (kMasked && (ko < jlo || ko > jhi)) pr = 0.0f;
           dpacc[r] = pr * (kNdl ? dpacc[r] : dpacc[r] - dl);

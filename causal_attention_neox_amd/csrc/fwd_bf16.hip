@@ -160,9 +160,10 @@ struct TilePlan {
         const int P = 64 * blk + lane;
         const int row = P / CPR;
         const int r = min(k0 + row, S - 1) - k0;
-        dma16(vr, 2u * (uint32_t)(r * vs + 8 * ((P % CPR) ^ Swz<D>::v(row))), Vt + 512 * blk);
+        dma16(vr, 2u * (uint32_t)(r * (int)vs + 8 * ((P % CPR) ^ Swz<D>::v(row))), Vt + 512 * blk);
         if (kdirect & (1 << i))
-          dma16(kr, 2u * (uint32_t)(r * ks + 8 * ((P % CPR) ^ Swz<D>::k(row))), Kt + 512 * blk);
+          dma16(kr, 2u * (uint32_t)(r * (int)ks + 8 * ((P % CPR) ^ Swz<D>::k(row))),
+                Kt + 512 * blk);
       }
     }
     const int half = rd >> 1;
@@ -482,7 +483,8 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
     for (int i = 0; i < CPR / 2; ++i) {
       const int P = 64 * i + lane, row = P / CPR;
       const int ch = (P % CPR) ^ (row & QSW);
-      dma16(qr, 2u * (uint32_t)((min(r0 + row, S - 1) - rb) * p.sq.s + 8 * ch), qrows + 512 * i);
+      dma16(qr, 2u * (uint32_t)((min(r0 + row, S - 1) - rb) * (int)p.sq.s + 8 * ch),
+            qrows + 512 * i);
     }
   } else {
     const uint16_t* qrow = qb + (int64_t)qc * p.sq.s;
