@@ -318,8 +318,9 @@ struct FwdState {
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            sacc[blk][r] = __builtin_fmaf(sacc[blk][r], c2,
-                                          base + sl2 * (float)(32 * blk + 8 * (r >> 2) + (r & 3)));
+            sacc[blk][r] = __builtin_fmaf(
+                sacc[blk][r], c2,
+                __builtin_fmaf(sl2, (float)(32 * blk + 8 * (r >> 2) + (r & 3)), base));
       }
       if (need_mask) {
         const int jlo = lo - k0 - 4 * hh, jhi = hi - k0 - 4 * hh;  // allowed key offsets
