@@ -328,16 +328,20 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NB; ++db)
       taddr[s2][db] = 8 * ((trow + 8 * s2) * C + ((4 * db + tch) ^ swz<C>(trow + 8 * s2))) +
-                      thalf + 32 * qhalf * D;
+                      thalf + 32 * qhalf * D + L::Q0;
   // Row-read offsets: Q~ / dO row 32 qhalf + ql (the second quarter adds the
-  // constant 64 rows), K~ / V row 32 kg + ql.
+  // constant 64 rows), K~ / V row 32 kg + ql.  The Q~ offsets (rofs, taddr)
+  // are absolute element addresses of the current q-tile buffer: they move to
+  // the other buffer after every tile, so that each operand read is one
+  // register plus an immediate (the dO tiles sit a constant distance above).
   constexpr int NS = D / 16;  // dims steps of S and dP
   int rofs[NS], kofs[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) {
-    rofs[c] = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw));
+    rofs[c] = 8 * ((32 * qhalf + ql) * C + ((2 * c + hh) ^ rsw)) + L::Q0;
     kofs[c] = 8 * ((32 * kg + ql) * C + ((2 * c + hh) ^ rsw));
   }
+  constexpr int GQ = L::G0 - L::Q0;  // dO tile of a buffer, relative to its Q~ tile
 
   const float c2 = a.scale_log2;
   const float scale = a.scale;
@@ -349,12 +353,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     dkacc[db] = f32x16{};
   }
 
-  // One q-tile.  The LDS areas come in as distinct restrict pointers so that
-  // the compiler can tell the reads of this tile from the direct-to-LDS loads
-  // of the next one still in flight (otherwise every LDS read would first
-  // wait for all outstanding vector memory operations).
-  auto tile = [&](auto masked, int qt, const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Gt,
-                  uint16_t* __restrict__ Qn, const uint16_t* __restrict__ KTp,
+  // One q-tile (its Q~ / dO operands at the current rofs / taddr).
+  auto tile = [&](auto masked, int qt, uint16_t* __restrict__ Qn, const uint16_t* __restrict__ KTp,
                   const uint16_t* __restrict__ VTp, const float* __restrict__ Fc,
                   float* __restrict__ Fn) __attribute__((always_inline)) {
     const int q0 = qt * BMQ;
@@ -385,9 +385,9 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       // dO^T and Q~^T operands of (query chunk qc, dim block db): transposed
       // reads.
       constexpr int NG = 2 * NB;
-      auto top = [&](const uint16_t* T, int g) {
-        const int off = taddr[0][g % NB] + 16 * (g / NB) * D + 64 * R * D;
-        return tr8(T + off, taddr[1][g % NB] - taddr[0][g % NB]);
+      auto top = [&](int base, int g) {
+        const int off = taddr[0][g % NB] + base + 16 * (g / NB) * D + 64 * R * D;
+        return tr8(lds + off, taddr[1][g % NB] - taddr[0][g % NB]);
       };
       // One stream of MFMA steps: S (NS), dP (NS), dV (NG), dK (NG); each
       // step's LDS operands are read PF steps ahead.
@@ -399,16 +399,16 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       auto rd = [&](int t) {
         Op o;
         if (t < NS) {
-          o.a = lds_read8(Qt + rofs[t] + RQ);
+          o.a = lds_read8(lds + rofs[t] + RQ);
           o.b = kRegK ? o.a : lds_read8(KTp + kofs[t]);
         } else if (t < 2 * NS) {
-          o.a = lds_read8(Gt + rofs[t - NS] + RQ);
+          o.a = lds_read8(lds + GQ + rofs[t - NS] + RQ);
           o.b = kRegV ? o.a : lds_read8(VTp + kofs[t - NS]);
         } else if (t < 2 * NS + NG) {
-          o.a = top(Gt, t - 2 * NS);
+          o.a = top(GQ, t - 2 * NS);
           o.b = o.a;
         } else {
-          o.a = top(Qt, t - 2 * NS - NG);
+          o.a = top(0, t - 2 * NS - NG);
           o.b = o.a;
         }
         return o;
@@ -489,9 +489,16 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   };
   auto run = [&](auto masked, int qt) __attribute__((always_inline)) {
     const int buf = (qt - qt_lo) & 1;
-    tile(masked, qt, lds + L::Q0 + buf * BMQ * D, lds + L::G0 + buf * BMQ * D,
-         lds + L::Q0 + (buf ^ 1) * BMQ * D, lds + L::KT, lds + L::VT, fl + buf * BMQ,
+    tile(masked, qt, lds + L::Q0 + (buf ^ 1) * BMQ * D, lds + L::KT, lds + L::VT, fl + buf * BMQ,
          fl + (buf ^ 1) * BMQ);
+    // the next tile's operands sit in the other buffer
+    const int step = buf ? -BMQ * D : BMQ * D;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) rofs[c] += step;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < NB; ++db) taddr[s2][db] += step;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
