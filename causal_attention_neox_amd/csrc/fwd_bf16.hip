@@ -4,7 +4,7 @@
 // Tiled, IO-aware exact attention (the FlashAttention-2 form the GPT-NeoX pages
 // name in "GPT-NeoX 开源训练框架深度解读", section "问题二：注意力计算太慢"):
 // each workgroup owns 128 query rows of one (batch, head); it streams K/V in
-// tiles of 64 keys through LDS, keeps a running row max and row sum (online
+// tiles of 64 keys (32 at D = 128) through LDS, keeps a running row max and row sum (online
 // softmax) in registers, and never materialises the S x S score matrix.  The
 // NeoX rotary rotation of Q and K ("FasterTransformer GPT-NeoX 推理指南",
 // neox_rotary_style_ / rotary_embedding) is applied while rows are loaded.
@@ -43,11 +43,26 @@ namespace NEOX_ELEM_NS {
 namespace {
 
 constexpr int BM = 128;  // query rows per workgroup (4 waves x 32)
-constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
-// A lane's probabilities over one tile (its 32 keys) may sum to at most 2^8
-// before the exact path raises the running max, so each stays <= 2^8.
+// A lane's probabilities over one tile (its keys of the tile) may sum to at
+// most 2^8 before the exact path raises the running max, so each stays <= 2^8.
 constexpr float kTileSumLimit = 256.0f;
+
+#ifndef NEOX_FWD_BN128
+#define NEOX_FWD_BN128 32
+#endif
+// K/V tile geometry per head dim.  At D = 128 a tile holds 32 keys: the
+// smaller score block and LDS footprint let three workgroups share a CU (at
+// most 168 registers per lane, 48 KB of LDS each), one more than 64-key tiles
+// allow there.  LDS holds two buffers of (K, V), each K tile followed by its
+// V tile; Q~ rows are staged after the first pair during the prologue.
+template <int D>
+struct FwdTile {
+  static constexpr int BN = D == 128 ? NEOX_FWD_BN128 : 64;  // keys per tile
+  static constexpr int KB = BN / 32;                          // 32-key score blocks per tile
+  static constexpr int TILE = BN * D;                         // elements of one K or V buffer
+  static constexpr int LDS = 2 * TILE + (2 * TILE > BM * D ? 2 * TILE : BM * D);
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -81,8 +96,9 @@ struct Swz {
 // (rotated element-wise).
 template <int D, int ROT>
 struct TilePlan {
+  static constexpr int BN = FwdTile<D>::BN;
   static constexpr int CPR = D / 8;             // chunks per row
-  static constexpr int NB = CPR / 4;            // direct-load blocks per wave (of K and of V)
+  static constexpr int NB = BN * CPR / 256;     // direct-load blocks per wave (of K and of V)
   static constexpr bool PAIRS = ROT == 1 || ROT == 2;
   static constexpr int W = ROT == 1 ? 8 : 4;    // pairs per pair item
   static constexpr int NPAIR = PAIRS ? (BN * D / (2 * W) + NT - 1) / NT : 1;
@@ -254,7 +270,9 @@ struct TilePlan {
 template <int D, int ROT, bool ALIBI>
 struct FwdState {
   static constexpr int CPR = D / 8;
-  static constexpr int TILE = BN * D;
+  static constexpr int BN = FwdTile<D>::BN;
+  static constexpr int KB = FwdTile<D>::KB;
+  static constexpr int TILE = FwdTile<D>::TILE;
   uint16_t* lds;
   TilePlan<D, ROT> tp;
   elem8 qreg[D / 16];
@@ -263,17 +281,18 @@ struct FwdState {
   // LDS element offsets of this lane's operand reads, from the start of a
   // K or V tile buffer.
   int kaddr[D / 16];     // K~ A operand, rows 0..31 (per chunk pair); rows 32..63
-                         // use the same swizzle, 32 * D elements further
+                         // (a second score block) use the same swizzle, 32 * D
+                         // elements further
   int vaddr[D / 32];     // V^T transposed reads (per dim block)
   int lo, hi, qi, hh, wave;
   float c2, sl2;
 
-  // One 64-key tile read from LDS buffer `buf`; fetches the next tile (if any)
-  // into the other buffer meanwhile.
+  // One tile read from LDS buffer pair `buf`; fetches the next tile (if any)
+  // into the other pair meanwhile.
   __device__ __forceinline__ void step(const FwdParams& p, const uint16_t* kb,
                                        const uint16_t* vb, int kt, int kt_hi, int buf) {
-    body(p, kb, vb, kt, kt_hi, lds + buf * TILE, lds + (2 + buf) * TILE, lds + (1 - buf) * TILE,
-         lds + (3 - buf) * TILE);
+    body(p, kb, vb, kt, kt_hi, lds + buf * 2 * TILE, lds + buf * 2 * TILE + TILE,
+         lds + (1 - buf) * 2 * TILE, lds + (1 - buf) * 2 * TILE + TILE);
   }
   // The tile buffers come in as distinct restrict pointers, so the compiler
   // knows the operand reads of this tile do not alias the direct-to-LDS loads
@@ -293,21 +312,25 @@ struct FwdState {
     if (__any(lane_any)) {
       const bool lane_full = (k0 >= lo) && (k0 + BN - 1 <= hi);
       const bool need_mask = !__all(lane_full);
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      f32x16 sacc[KB];
+#pragma unroll
+      for (int blk = 0; blk < KB; ++blk) sacc[blk] = f32x16{};
       // K~ operands are read one dims step ahead of the MFMAs using them.
-      elem8 k0c = lds_read8(Kc + kaddr[0]), k1c = lds_read8(Kc + kaddr[0] + 32 * D);
+      elem8 kc[KB];
+#pragma unroll
+      for (int blk = 0; blk < KB; ++blk) kc[blk] = lds_read8(Kc + kaddr[0] + 32 * D * blk);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        elem8 k0n = k0c, k1n = k1c;
-        if (c + 1 < D / 16) {
-          k0n = lds_read8(Kc + kaddr[c + 1]);
-          k1n = lds_read8(Kc + kaddr[c + 1] + 32 * D);
-        }
+        elem8 kn[KB];
+#pragma unroll
+        for (int blk = 0; blk < KB; ++blk)
+          kn[blk] = c + 1 < D / 16 ? lds_read8(Kc + kaddr[c + 1] + 32 * D * blk) : kc[blk];
         __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
-        sacc[0] = mfma32x32x16(k0c, qreg[c], sacc[0]);
-        sacc[1] = mfma32x32x16(k1c, qreg[c], sacc[1]);
-        k0c = k0n;
-        k1c = k1n;
+#pragma unroll
+        for (int blk = 0; blk < KB; ++blk) {
+          sacc[blk] = mfma32x32x16(kc[blk], qreg[c], sacc[blk]);
+          kc[blk] = kn[blk];
+        }
       }
       // Register r of block blk: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.  The
       // scores stay in the accumulator registers: raw (RoPE) or exp2-domain
@@ -315,7 +338,7 @@ struct FwdState {
       if (ALIBI) {
         const float base = sl2 * (float)(k0 + 4 * hh - qi);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < KB; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             sacc[blk][r] = __builtin_fmaf(
@@ -325,7 +348,7 @@ struct FwdState {
       if (need_mask) {
         const int jlo = lo - k0 - 4 * hh, jhi = hi - k0 - 4 * hh;  // allowed key offsets
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < KB; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = 32 * blk + 8 * (r >> 2) + (r & 3);
@@ -361,11 +384,12 @@ struct FwdState {
         exact = __any(ts > kTileSumLimit);
       }
       if (exact) {
+        constexpr int NSC = 16 * KB;  // this lane's scores of the tile
         float mx = fmaxf(sacc[0][0], fmaxf(sacc[0][1], sacc[0][2]));
 #pragma unroll
-        for (int i = 3; i < 31; i += 2)
+        for (int i = 3; i + 1 < NSC; i += 2)
           mx = fmaxf(mx, fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
-        mx = fmaxf(mx, sacc[1][15]);
+        mx = fmaxf(mx, sacc[KB - 1][15]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mt = ALIBI ? mx : mx * c2;  // tile max in the exp2 domain
         const float m_new = fmaxf(m_ref, mt);
@@ -401,11 +425,11 @@ struct FwdState {
 };
 
 // Workgroups per CU the register budget is sized for: 3 (at most 168
-// registers per lane) for the plain-K form at D <= 96, else 2.  The rotating
-// forms need more registers.
+// registers per lane) for the plain-K form at D <= 96 and with 32-key tiles,
+// else 2.  The rotating forms need more registers.
 template <int D, int ROT>
 struct FwdOccupancy {
-  static constexpr int value = (ROT == 0 && D <= 96) ? 3 : 2;
+  static constexpr int value = (ROT == 0 && (D <= 96 || FwdTile<D>::BN == 32)) ? 3 : 2;
 };
 
 // ROT: how K tiles are staged (0: plain or pre-rotated K; 1, 2: rotary pair
@@ -413,8 +437,9 @@ struct FwdOccupancy {
 template <int D, int ROT, bool ALIBI, bool QROT>
 __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_kernel(FwdParams p) {
   constexpr int CPR = D / 8;
-  constexpr int TILE = BN * D;  // elements per tile buffer (unpadded, swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
+  constexpr int BN = FwdTile<D>::BN;
+  constexpr int TILE = FwdTile<D>::TILE;  // elements per tile buffer (unpadded, swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[FwdTile<D>::LDS];  // K0 V0 K1 V1 (+ Q~ staging)
 
   const AttnShape& a = p.a;
   const int S = a.S;
@@ -466,16 +491,16 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
 
   // Prologue: fetch the first tile while Q~ is being loaded.
   st.tp.init(wave, lane, tid, a.rd, p.sk.s, p.sv.s);
-  st.tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + 2 * TILE, wave);
+  st.tp.fetch(kb, p.sk.s, vb, p.sv.s, kt_lo * BN, S, a.rd, lds, lds + TILE, wave);
 
   // Q~ of this lane's row as the B operand: chunk c holds dims 16c + 8hh .. +7.
   // Rotation-free: the wave's 32 rows are loaded whole (16 bytes per lane, D / 8
-  // lanes per row, rows past S clamped) straight into a free part of the
-  // second tile buffer, chunk c of row r at position c ^ (r & QSW) (row-wise
-  // writes and column-wise reads both conflict-free), and read back in the
-  // operand layout after the prologue barrier.
+  // lanes per row, rows past S clamped) straight into LDS past the first
+  // tile pair, chunk c of row r at position c ^ (r & QSW) (row-wise writes and
+  // column-wise reads both conflict-free), and read back in the operand
+  // layout after the prologue barrier.
   constexpr int QSW = CPR == 16 ? 15 : (CPR == 8 ? 7 : 3);
-  uint16_t* qrows = lds + ((wave & 2) ? 3 * TILE : TILE) + (wave & 1) * 32 * D;
+  uint16_t* qrows = lds + 2 * TILE + wave * 32 * D;
   if (ROT == 0 && !QROT) {
     const int r0 = q0 + wave * 32;
     const int rb = min(r0, S - 1);  // rows past S re-read row S-1 (never stored)
@@ -564,6 +589,7 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
     // the loop; each wave uses its own 32 padded rows): whole rows out, 16
     // bytes per lane, instead of 16-byte pieces of 32 rows per store.
     constexpr int RS = D + 8;
+    static_assert(4 * 32 * RS <= FwdTile<D>::LDS, "o staging exceeds the LDS array");
     uint16_t* orows = lds + wave * 32 * RS;
     // The lane index passes through an empty asm here, so the address
     // arithmetic below is not hoisted above the loop (where registers are
