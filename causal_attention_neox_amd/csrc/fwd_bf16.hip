@@ -48,9 +48,6 @@ constexpr int NT = 256;  // threads per workgroup
 // most 2^8 before the exact path raises the running max, so each stays <= 2^8.
 constexpr float kTileSumLimit = 256.0f;
 
-#ifndef NEOX_FWD_BN128
-#define NEOX_FWD_BN128 32
-#endif
 // K/V tile geometry per head dim.  At D = 128 a tile holds 32 keys: the
 // smaller score block and LDS footprint let three workgroups share a CU (at
 // most 168 registers per lane, 48 KB of LDS each), one more than 64-key tiles
@@ -58,7 +55,7 @@ constexpr float kTileSumLimit = 256.0f;
 // V tile; Q~ rows are staged after the first pair during the prologue.
 template <int D>
 struct FwdTile {
-  static constexpr int BN = D == 128 ? NEOX_FWD_BN128 : 64;  // keys per tile
+  static constexpr int BN = D == 128 ? 32 : 64;  // keys per tile
   static constexpr int KB = BN / 32;                          // 32-key score blocks per tile
   static constexpr int TILE = BN * D;                         // elements of one K or V buffer
   static constexpr int LDS = 2 * TILE + (2 * TILE > BM * D ? 2 * TILE : BM * D);
@@ -99,6 +96,7 @@ struct TilePlan {
   static constexpr int BN = FwdTile<D>::BN;
   static constexpr int CPR = D / 8;             // chunks per row
   static constexpr int NB = BN * CPR / 256;     // direct-load blocks per wave (of K and of V)
+  static_assert(BN * CPR % 256 == 0, "a tile is whole 1 KB blocks for every wave");
   static constexpr bool PAIRS = ROT == 1 || ROT == 2;
   static constexpr int W = ROT == 1 ? 8 : 4;    // pairs per pair item
   static constexpr int NPAIR = PAIRS ? (BN * D / (2 * W) + NT - 1) / NT : 1;
