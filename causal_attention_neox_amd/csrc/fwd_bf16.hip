@@ -20,8 +20,9 @@
 //  * K/V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds) into an
 //    unpadded, XOR-swizzled layout that keeps the operand reads free of bank
 //    conflicts; only the rotary dims of K pass through registers.  Two LDS
-//    buffers, one barrier per tile; every LDS operand address is a per-lane
-//    register offset from the buffer's base plus an immediate.
+//    buffers (three for 32-key tiles), one barrier per tile; every LDS operand
+//    address is a per-lane register offset from the buffer's base plus an
+//    immediate.
 //  * Tiles fully inside every row's allowed range skip the mask.  A tile's
 //    probabilities are taken against the running max without first finding
 //    the tile's own max; their per-lane sum bounds each of them, and only a
@@ -264,6 +265,31 @@ struct TilePlan {
   }
 };
 
+// Workgroups per CU the register budget is sized for: 3 (at most 168
+// registers per lane) for the plain-K form at D <= 96 and with 32-key tiles,
+// else 2.  The rotating forms need more registers.
+template <int D, int ROT>
+struct FwdOccupancy {
+  static constexpr int value = (ROT == 0 && (D <= 96 || FwdTile<D>::BN == 32)) ? 3 : 2;
+};
+
+// (K, V) buffer pairs: three for the plain-K form with 32-key tiles, whose
+// third pair fits in the LDS the Q~ staging needs anyway (tiles then load two
+// ahead, and the end-of-tile wait leaves the newest tile's loads in flight),
+// else two.  (With 64-key tiles at D = 64 a third pair fits too but measured
+// no faster.)
+template <int D, int ROT>
+struct FwdBuffers {
+  static constexpr int value = (ROT == 0 && FwdTile<D>::BN == 32) ? 3 : 2;
+  static constexpr int LDS = FwdTile<D>::LDS > 2 * value * FwdTile<D>::TILE
+                                 ? FwdTile<D>::LDS
+                                 : 2 * value * FwdTile<D>::TILE;
+};
+
+// s_waitcnt immediate (gfx9 encoding): at most n vector memory loads still
+// outstanding, all LDS operations done, expcnt not waited on.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
 // State of one workgroup's forward pass (one wave's view).
 template <int D, int ROT, bool ALIBI>
 struct FwdState {
@@ -271,6 +297,7 @@ struct FwdState {
   static constexpr int BN = FwdTile<D>::BN;
   static constexpr int KB = FwdTile<D>::KB;
   static constexpr int TILE = FwdTile<D>::TILE;
+  static constexpr int NBUF = FwdBuffers<D, ROT>::value;
   uint16_t* lds;
   TilePlan<D, ROT> tp;
   elem8 qreg[D / 16];
@@ -285,12 +312,13 @@ struct FwdState {
   int lo, hi, qi, hh, wave;
   float c2, sl2;
 
-  // One tile read from LDS buffer pair `buf`; fetches the next tile (if any)
-  // into the other pair meanwhile.
+  // One tile read from LDS buffer pair `buf`; fetches tile kt + NBUF - 1 (if
+  // any) into the pair read by the previous tile meanwhile.
   __device__ __forceinline__ void step(const FwdParams& p, const uint16_t* kb,
                                        const uint16_t* vb, int kt, int kt_hi, int buf) {
+    const int nb = buf == 0 ? NBUF - 1 : buf - 1;
     body(p, kb, vb, kt, kt_hi, lds + buf * 2 * TILE, lds + buf * 2 * TILE + TILE,
-         lds + (1 - buf) * 2 * TILE, lds + (1 - buf) * 2 * TILE + TILE);
+         lds + nb * 2 * TILE, lds + nb * 2 * TILE + TILE);
   }
   // The tile buffers come in as distinct restrict pointers, so the compiler
   // knows the operand reads of this tile do not alias the direct-to-LDS loads
@@ -303,8 +331,9 @@ struct FwdState {
     const AttnShape& a = p.a;
     const int S = a.S;
     const int k0 = kt * BN;
-    const bool more = kt + 1 < kt_hi;
-    if (more) tp.fetch(kb, p.sk.s, vb, p.sv.s, k0 + BN, S, a.rd, Kn, Vn, wave);
+    const int kf = k0 + (NBUF - 1) * BN;  // first key of the tile fetched now
+    const bool more = kt + NBUF - 1 < kt_hi;
+    if (more) tp.fetch(kb, p.sk.s, vb, p.sv.s, kf, S, a.rd, Kn, Vn, wave);
 
     const bool lane_any = (k0 <= hi) && (k0 + BN - 1 >= lo);
     if (__any(lane_any)) {
@@ -416,18 +445,24 @@ struct FwdState {
         vcur = vnext;
       }
     }
-    if (more) tp.store(Kn, kb, p.sk.s, k0 + BN, S, a.rd, a.rope);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (more) tp.store(Kn, kb, p.sk.s, kf, S, a.rd, a.rope);
+    if (NBUF == 3) {
+      // Wait for the next tile's loads only, then the barrier without the
+      // release fence of __syncthreads (which, even for LDS alone, would wait
+      // for the direct-to-LDS loads still in flight); the acquire fence keeps
+      // the next tile's LDS reads below the barrier.
+      if (more)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * TilePlan<D, ROT>::NB));
+      else
+        __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
-};
-
-// Workgroups per CU the register budget is sized for: 3 (at most 168
-// registers per lane) for the plain-K form at D <= 96 and with 32-key tiles,
-// else 2.  The rotating forms need more registers.
-template <int D, int ROT>
-struct FwdOccupancy {
-  static constexpr int value = (ROT == 0 && (D <= 96 || FwdTile<D>::BN == 32)) ? 3 : 2;
 };
 
 // ROT: how K tiles are staged (0: plain or pre-rotated K; 1, 2: rotary pair
@@ -437,7 +472,8 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
   constexpr int CPR = D / 8;
   constexpr int BN = FwdTile<D>::BN;
   constexpr int TILE = FwdTile<D>::TILE;  // elements per tile buffer (unpadded, swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[FwdTile<D>::LDS];  // K0 V0 K1 V1 (+ Q~ staging)
+  constexpr int NBUF = FwdBuffers<D, ROT>::value;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[FwdBuffers<D, ROT>::LDS];  // K0 V0 K1 V1 .. (+ Q~ staging)
 
   const AttnShape& a = p.a;
   const int S = a.S;
@@ -553,6 +589,9 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
       st.qreg[c] = qi < S ? lds_read8(qrows + ql * D + 8 * ((2 * c + hh) ^ (ql & QSW))) : elem8{};
     __syncthreads();  // every wave has its Q~ before the first fetch reuses the buffer
   }
+  if (NBUF == 3 && kt_lo + 1 < kt_hi)
+    st.tp.fetch(kb, p.sk.s, vb, p.sv.s, (kt_lo + 1) * BN, S, a.rd, lds + 2 * TILE, lds + 3 * TILE,
+                wave);
 
   st.sl2 = ALIBI ? alibi_slope_log2(a, h) : 0.0f;
   st.c2 = a.scale_log2;
@@ -561,7 +600,11 @@ __global__ __launch_bounds__(NT, (FwdOccupancy<D, ROT>::value)) void fwd_bf16_ke
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.oacc[db] = f32x16{};
 
-  for (int kt = kt_lo; kt < kt_hi; ++kt) st.step(p, kb, vb, kt, kt_hi, (kt - kt_lo) & 1);
+  int buf = 0;
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    st.step(p, kb, vb, kt, kt_hi, buf);
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
+  }
 
   // Epilogue: o = O / l, lse = (m + log2 l) ln 2.
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
