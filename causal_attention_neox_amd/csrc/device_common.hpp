@@ -243,6 +243,10 @@ struct RowGroups {
   static constexpr int RPB = 4 * RPW; // rows per 256-thread workgroup
 };
 
+// s_waitcnt immediate (gfx9 encoding): at most n vector memory loads still
+// outstanding, all LDS operations done, expcnt not waited on.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
 // Waits for this wave's LDS operations only (lgkmcnt(0); vmcnt and expcnt
 // left at their maxima in the gfx9 s_waitcnt encoding).
 __device__ __forceinline__ void lds_wave_sync() {

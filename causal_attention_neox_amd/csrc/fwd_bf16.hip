@@ -286,10 +286,6 @@ struct FwdBuffers {
                                  : 2 * value * FwdTile<D>::TILE;
 };
 
-// s_waitcnt immediate (gfx9 encoding): at most n vector memory loads still
-// outstanding, all LDS operations done, expcnt not waited on.
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
-
 // State of one workgroup's forward pass (one wave's view).
 template <int D, int ROT, bool ALIBI>
 struct FwdState {
