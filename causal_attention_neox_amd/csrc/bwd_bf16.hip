@@ -502,10 +502,12 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  // masked and unmasked runs of q-tiles (each form's code appears once)
   int qt = qt_lo;
-  for (; qt < qt_hi && !full(qt); ++qt) run(std::true_type{}, qt);
-  for (; qt < qt_hi && full(qt); ++qt) run(std::false_type{}, qt);
-  for (; qt < qt_hi; ++qt) run(std::true_type{}, qt);
+  while (qt < qt_hi) {
+    for (; qt < qt_hi && !full(qt); ++qt) run(std::true_type{}, qt);
+    for (; qt < qt_hi && full(qt); ++qt) run(std::false_type{}, qt);
+  }
 
   // Epilogue: the two query halves of a key group add their dK~ and dV partial
   // sums in fp32 over the (now idle) LDS, then rows are written coalesced;
@@ -519,6 +521,12 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto epilogue = [&](auto rope_tag) __attribute__((always_inline)) {
     constexpr bool kRope = decltype(rope_tag)::value;
     const int rd = a.rd, half = rd >> 1;
+    // This lane's staged row, derived here from the thread index (through an
+    // empty asm, so that it is not computed before the tile loop and kept
+    // live across it).
+    int te = tid;
+    __asm__ volatile("" : "+v"(te));
+    const int erow = 32 * kg + (te & 31);
     // Query half 1 stores its sums, query half 0 adds its own (all reads
     // issued before the first add) and stores the total.
     if (qhalf == 1) {
@@ -526,7 +534,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
       for (int db = 0; db < NB; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int off = (32 * kg + ql) * FS + 32 * db + 8 * a4 + 4 * hh;
+          const int off = erow * FS + 32 * db + 8 * a4 + 4 * hh;
           f32x4 wk, wv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -547,8 +555,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int db = 0; db < NB; ++db)
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4)
-            o4[db][a4] = *reinterpret_cast<const f32x4*>(st + (32 * kg + ql) * FS + 32 * db +
-                                                         8 * a4 + 4 * hh);
+            o4[db][a4] = *reinterpret_cast<const f32x4*>(st + erow * FS + 32 * db + 8 * a4 + 4 * hh);
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
             for (int e = 0; e < 4; ++e)
               w[e] = pass == 0 ? (dkacc[db][4 * a4 + e] + o4[db][a4][e]) * scale
                                : dvacc[db][4 * a4 + e] + o4[db][a4][e];
-            *reinterpret_cast<f32x4*>(st + (32 * kg + ql) * FS + 32 * db + 8 * a4 + 4 * hh) = w;
+            *reinterpret_cast<f32x4*>(st + erow * FS + 32 * db + 8 * a4 + 4 * hh) = w;
           }
       }
     }
