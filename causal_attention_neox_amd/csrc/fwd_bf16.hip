@@ -711,14 +711,35 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(FwdParams p) {
           x[2 * e] = el_lo(w[n][t][e]);
           x[2 * e + 1] = el_hi(w[n][t][e]);
         }
+        const uint16_t* prow = rowbuf[wave][n][rw][t];
+        if ((rd & 7) == 0) {
+          // The chunk lies inside the rotary dims, and half is a multiple of 4:
+          // each 4-dim group of it has its partners in one 8-byte-aligned
+          // group on the other side of half, read whole; rotate-half negates
+          // the partners of the first half (sign bits flipped in place).
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = d0 + e;
-          if (d < rd) {
-            const bool first = d < half;
-            const float sn = first ? -cs[e].y : cs[e].y;  // rotate-half: (-x2, x1)
-            x[e] = fmaf(el2f(rowbuf[wave][n][rw][t][first ? d + half : d - half]), sn,
-                        x[e] * cs[e].x);
+          for (int g4 = 0; g4 < 2; ++g4) {
+            const int ds = d0 + 4 * g4;
+            const bool first = ds < half;
+            const u32x2 pw = *reinterpret_cast<const u32x2*>(prow + (first ? ds + half : ds - half));
+            const uint32_t flip = first ? 0x80008000u : 0u;
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const uint32_t pv = pw[e2] ^ flip;
+              const int e = 4 * g4 + 2 * e2;
+              x[e] = fmaf(el_lo(pv), cs[e].y, x[e] * cs[e].x);
+              x[e + 1] = fmaf(el_hi(pv), cs[e + 1].y, x[e + 1] * cs[e + 1].x);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = d0 + e;
+            if (d < rd) {
+              const bool first = d < half;
+              const float sn = first ? -cs[e].y : cs[e].y;  // rotate-half: (-x2, x1)
+              x[e] = fmaf(el2f(prow[first ? d + half : d - half]), sn, x[e] * cs[e].x);
+            }
           }
         }
         w[n][t] = u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
