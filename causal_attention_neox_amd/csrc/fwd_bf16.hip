@@ -338,22 +338,26 @@ struct FwdState {
       f32x16 sacc[KB];
 #pragma unroll
       for (int blk = 0; blk < KB; ++blk) sacc[blk] = f32x16{};
-      // K~ operands are read one dims step ahead of the MFMAs using them.
-      elem8 kc[KB];
+      // K~ operands are read PF dims steps ahead of the MFMAs using them (two
+      // with one score block, so that a read has two products' time to land;
+      // one in the ALiBi form, whose bias terms leave no registers for it).
+      constexpr int NS = D / 16, PF = (KB == 1 && !ALIBI) ? 2 : 1;
+      elem8 kq[PF + 1][KB];
 #pragma unroll
-      for (int blk = 0; blk < KB; ++blk) kc[blk] = lds_read8(Kc + kaddr[0] + 32 * D * blk);
+      for (int s = 0; s < PF; ++s)
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        elem8 kn[KB];
+        for (int blk = 0; blk < KB; ++blk) kq[s][blk] = lds_read8(Kc + kaddr[s] + 32 * D * blk);
 #pragma unroll
-        for (int blk = 0; blk < KB; ++blk)
-          kn[blk] = c + 1 < D / 16 ? lds_read8(Kc + kaddr[c + 1] + 32 * D * blk) : kc[blk];
+      for (int c = 0; c < NS; ++c) {
+        if (c + PF < NS) {
+#pragma unroll
+          for (int blk = 0; blk < KB; ++blk)
+            kq[(c + PF) % (PF + 1)][blk] = lds_read8(Kc + kaddr[c + PF] + 32 * D * blk);
+        }
         __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
 #pragma unroll
-        for (int blk = 0; blk < KB; ++blk) {
-          sacc[blk] = mfma32x32x16(kc[blk], qreg[c], sacc[blk]);
-          kc[blk] = kn[blk];
-        }
+        for (int blk = 0; blk < KB; ++blk)
+          sacc[blk] = mfma32x32x16(kq[c % (PF + 1)][blk], qreg[c], sacc[blk]);
       }
       // Register r of block blk: key k0 + 32 blk + 8 (r/4) + 4 hh + r%4.  The
       // scores stay in the accumulator registers: raw (RoPE) or exp2-domain
