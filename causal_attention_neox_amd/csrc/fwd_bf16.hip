@@ -436,13 +436,15 @@ struct FwdState {
         const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
         return __builtin_bit_cast(elem8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      elem8 vcur = vread(0);
+      constexpr int PV = PF;  // MFMAs ahead
+      elem8 vq[PV + 1];
+#pragma unroll
+      for (int g = 0; g < PV; ++g) vq[g] = vread(g);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const elem8 vnext = g + 1 < NG ? vread(g + 1) : vcur;
+        if (g + PV < NG) vq[(g + PV) % (PV + 1)] = vread(g + PV);
         __builtin_amdgcn_sched_barrier(0);  // keep the next operands' reads ahead of these MFMAs
-        oacc[g % NDB] = mfma32x32x16(vcur, pb[g / NDB], oacc[g % NDB]);
-        vcur = vnext;
+        oacc[g % NDB] = mfma32x32x16(vq[g % (PV + 1)], pb[g / NDB], oacc[g % NDB]);
       }
     }
     if (more) tp.store(Kn, kb, p.sk.s, kf, S, a.rd, a.rope);
