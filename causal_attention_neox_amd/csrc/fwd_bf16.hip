@@ -428,7 +428,7 @@ struct FwdState {
         expo(m_ref == -INFINITY ? 0.0f : m_ref);
       }
       l_run += ts;
-      // V^T operands are read one MFMA ahead of their use.
+      // V^T operands are read PV products ahead of their use.
       constexpr int NDB = D / 32, NG = (BN / 16) * NDB;
       auto vread = [&](int g) {
         const uint16_t* vp = Vc + vaddr[g % NDB] + 16 * (g / NDB) * 8 * CPR;
@@ -436,7 +436,7 @@ struct FwdState {
         const s16x4 v1 = lds_read_tr4(vp + 8 * 8 * CPR);
         return __builtin_bit_cast(elem8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int PV = PF;  // MFMAs ahead
+      constexpr int PV = !ALIBI ? 2 : 1;  // MFMAs ahead
       elem8 vq[PV + 1];
 #pragma unroll
       for (int g = 0; g < PV; ++g) vq[g] = vread(g);
