@@ -455,25 +455,30 @@ def run_gpu(args, torch, np, neox, W, wl, inp):
     neox.neox_rope_table_prepare(S, kw["rotary_dim"], wl.rope_base)
 
     def step(ev):
-        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=ws, phase_events=ev[0:3], **kw)
+        neox.neox_attn_fwd_ex(q, k, v, o, lse, workspace=ws,
+                              phase_events=None if ev is None else ev[0:3], **kw)
         neox.neox_attn_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, workspace=ws,
-                              phase_events=ev[3:7], reuse_rotated_qk=True, **kw)
+                              phase_events=None if ev is None else ev[3:7],
+                              reuse_rotated_qk=True, **kw)
 
-    warm_ev = make_events(torch, 7)
     for _ in range(args.warmup):
-        step(warm_ev)
-    events = [make_events(torch, 7) for _ in range(args.steps)]
+        step(None)
+    # Phase events (per-kernel times) on every `stride`-th step of the timed
+    # steps: recording seven live events per step can make the host, not the
+    # GPU, set the pace of the loop.
+    stride = max(1, args.steps // 10)
+    events = {s: make_events(torch, 7) for s in range(0, args.steps, stride)}
     start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
     for s in range(args.steps):
-        step(events[s])
+        step(events.get(s))
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
 
     def avg(i, j):
-        return sum(ev[i].elapsed_time(ev[j]) for ev in events) / len(events)
+        return sum(ev[i].elapsed_time(ev[j]) for ev in events.values()) / len(events)
 
     # backward events: start, after the rotation pass (none here: q~ and k~ are
     # reused from the forward), after the dQ kernel (it also forms Delta and
