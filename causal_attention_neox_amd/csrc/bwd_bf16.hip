@@ -35,7 +35,6 @@ namespace neox {
 namespace NEOX_ELEM_NS {
 namespace {
 
-constexpr int BNK = 128;  // keys per dK/dV workgroup (4 key groups x 32)
 constexpr int NT = 256;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -135,21 +134,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------- dK / dV
 
-// Eight waves, two per SIMD.  Wave w owns the 32 keys 32 (w & 3) .. +31 of
-// the workgroup's 128 and query half w >> 2 (32 rows) of every 64-row q-tile;
-// the two waves of a key group add their dV / dK~ partial sums in the
-// epilogue.  At D <= 96 a q-tile has 128 rows and each wave takes two 32-row
-// quarters of it (rows 32 qhalf and 32 qhalf + 64) between barriers, which
-// halves the barriers and tile loads per row.  K~ and V are the B operands of
-// S and dP: held in registers at D = 64 (where they fit), else re-read from
-// stationary LDS tiles.
+// 2 KG waves, two waves per SIMD in all (KG key groups; two 4-wave
+// workgroups per CU at D <= 96, one 8-wave workgroup at D = 128).  Wave w
+// owns the 32 keys 32 (w % KG) .. +31 of the workgroup's 32 KG and query half
+// w / KG (32 rows) of every 64-row q-tile; the two waves of a key group add
+// their dV / dK~ partial sums in the epilogue.  (With 128-row q-tiles each
+// wave would take two 32-row quarters of a tile between barriers, halving the
+// barriers and tile loads per row; the layout keeps that form.)  K~ and V are
+// the B operands of S and dP: held in registers at D = 64 (where they fit),
+// else re-read from stationary LDS tiles.
 constexpr int kDkdvPrefetch = 1;  // MFMA steps between an LDS operand's read and its use
 
 template <int D>
 struct DkdvLds {
+  // Key groups of 32 keys per workgroup (two waves each, one per query half):
+  // two at D <= 96, where the LDS of a 64-key workgroup (64-row q-tiles)
+  // lets two workgroups share a CU, so that one's prologue and epilogue run
+  // beside the other's q-tiles; four at D = 128 (one workgroup per CU either
+  // way, and 128-key blocks halve the Q~ / dO tile loads).
+  static constexpr int KG = D <= 96 ? 2 : 4;
+  static constexpr int BNK = 32 * KG;   // keys per workgroup
+  static constexpr int NW = 2 * KG;     // waves per workgroup
+  static constexpr int NTH = 64 * NW;   // threads per workgroup
   // q-tile rows per barrier: 128 where the double-buffered tiles fit in LDS
   // (each wave then takes two 32-row quarters of a tile), else 64.
-  static constexpr int BMQ = D <= 96 ? 128 : 64;
+  static constexpr int BMQ = (D <= 96 && KG == 4) ? 128 : 64;
   static constexpr int NQQ = BMQ / 64;  // quarters per wave per tile
   static constexpr int C = D / 8;
   static constexpr bool kRegK = D <= 64;         // K~ B operands held in registers
@@ -164,19 +173,19 @@ struct DkdvLds {
   static constexpr int N16 = N16T * 2 > EPI_BYTES ? N16T : EPI_BYTES / 2;  // LDS, uint16 units
   static_assert((F0 * 2) % 16 == 0, "float area alignment");
 };
-constexpr int NT8 = 512;
-
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(DkdvLds<D>::NTH, 8 / DkdvLds<D>::NW) void bwd_dkdv_kernel(BwdParams p) {
   using L = DkdvLds<D>;
+  constexpr int BNK = L::BNK, NW = L::NW, KG = L::KG, NT8 = L::NTH;
   constexpr int BMQ = L::BMQ;
   constexpr int C = L::C;
   constexpr int NB = D / 32;
   constexpr int NQQ = L::NQQ;
   constexpr int CB = C * BMQ / 64;  // 1 KB blocks of one q-tile tensor (Q~ or dO)
-  constexpr int NFB = 2 * CB / 8;   // direct-load blocks per wave of a q-tile (Q~ and dO)
-  constexpr int NKB = 2 * C / 8;    // direct-load blocks per wave of the stationary K~ (or V)
-  static_assert((2 * C) % 8 == 0, "tile blocks must split evenly over 8 waves");
+  constexpr int NFB = 2 * CB / NW;  // direct-load blocks per wave of a q-tile (Q~ and dO)
+  constexpr int NKB = BNK * C / 64 / NW;  // direct-load blocks per wave of the stationary K~ (or V)
+  static_assert((2 * CB) % NW == 0 && (BNK * C / 64) % NW == 0,
+                "tile blocks must split evenly over the waves");
   constexpr bool kRegK = L::kRegK, kRegV = L::kRegV;
   __shared__ __attribute__((aligned(16))) uint16_t lds[L::N16];
   float* fl = reinterpret_cast<float*>(lds + L::F0);  // nlse[2][BMQ], delta[2][BMQ]
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int kg = wave & 3, qhalf = wave >> 2;
+  const int kg = wave % KG, qhalf = wave / KG;
   const int ql = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4, j16 = lane & 15;
   const int k0 = kt * BNK;
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
   bool fdo[NFB];
 #pragma unroll
   for (int n = 0; n < NFB; ++n) {
-    const int fbk = wave + 8 * n;
+    const int fbk = wave + NW * n;
     fdo[n] = fbk >= CB;
     const int blk = fdo[n] ? fbk - CB : fbk;
     const int P = 64 * blk + lane;
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     } else {
 #pragma unroll
       for (int n = 0; n < NFB; ++n) {
-        const int fbk = wave + 8 * n;
+        const int fbk = wave + NW * n;
         const int blk = fdo[n] ? fbk - CB : fbk;
         const int P = 64 * blk + lane;
         const int row = P / C, ch = (P % C) ^ swz<C>(row);
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv_kernel(BwdParams p) {
     const buf_rsrc vr = raw_rsrc(vb + (int64_t)k0 * p.sv.s);
 #pragma unroll
     for (int n = 0; n < NKB; ++n) {
-      const int blk = wave + 8 * n;
+      const int blk = wave + NW * n;
       const int P = 64 * blk + lane;
       const int row = P / C, ch = (P % C) ^ swz<C>(row);
       const int rr = min(k0 + row, S - 1) - k0;
@@ -1002,11 +1011,12 @@ hipError_t launch_d(const BwdParams& p, hipStream_t st, const hipEvent_t* ev) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(NT), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev, 2, st)) != hipSuccess) return e;
-  const dim3 kgrid((unsigned)((p.a.S + BNK - 1) / BNK) * BH);
+  using L = DkdvLds<D>;
+  const dim3 kgrid((unsigned)((p.a.S + L::BNK - 1) / L::BNK) * BH);
   if (plan.alibi)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(NT8), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(L::NTH), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(NT8), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(L::NTH), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev, 3, st);
 }
