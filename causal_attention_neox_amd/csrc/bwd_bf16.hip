@@ -489,9 +489,10 @@ __global__ __launch_bounds__(DkdvLds<D>::NTH, 8 / DkdvLds<D>::NW) void bwd_dkdv_
     quarter(std::integral_constant<int, 0>{});
     if constexpr (NQQ == 2) quarter(std::integral_constant<int, 1>{});
   };
-  // A wave's q-tiles fall into three runs: masked ones before its first tile
-  // inside every row's range (the diagonal), unmasked ones, masked ones after
-  // (document ends).  One loop per run keeps one variant of the tile per loop.
+  // A wave's q-tiles fall into runs: masked ones before its first tile inside
+  // every row's range (the diagonal), unmasked ones, masked ones after
+  // (document ends).  An inner loop per run keeps one variant of the tile per
+  // loop.
   auto full = [&](int qt) {
     const int qw0 = qt * BMQ + 32 * qhalf;  // first row of the wave's first quarter
     return __all((qw0 >= qlo) && (qw0 + 64 * (NQQ - 1) + 31 <= qhi));
