@@ -294,6 +294,9 @@ struct FwdState {
   static constexpr int KB = FwdTile<D>::KB;
   static constexpr int TILE = FwdTile<D>::TILE;
   static constexpr int NBUF = FwdBuffers<D, ROT>::value;
+  // The three-buffer wait counts this wave's direct loads of one tile; only
+  // the plain-K form issues no other vector memory loads inside the loop.
+  static_assert(NBUF == 2 || ROT == 0, "three buffers need the plain-K form");
   uint16_t* lds;
   TilePlan<D, ROT> tp;
   elem8 qreg[D / 16];
