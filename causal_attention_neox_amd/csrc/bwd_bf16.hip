@@ -17,8 +17,9 @@
 //          start from -Delta, so dP - Delta costs no extra step); 64-key
 //          tiles stream through LDS, S and dP are recomputed, dQ~ += dS' K~
 //          accumulates in registers, and the epilogue writes dq = scale R^T dQ~.
-//   dK/dV: one workgroup per (batch, head, 128 keys), K-stationary; 64-row
-//          q-tiles (with their Delta and nlse) stream through LDS:
+//   dK/dV: one workgroup per (batch, head, 64 keys; 128 at D = 128),
+//          K-stationary; 64-row q-tiles (with their Delta and nlse) stream
+//          through LDS:
 //            S = Q~ K~^T,  P = exp2(S scale log2e + nlse),  dP = dO V^T,
 //            dS' = P (dP - Delta),  dV^T += dO^T P,  dK~^T += Q~^T dS'.
 //          The epilogue writes dV and dK = scale R^T dK~.
