@@ -52,8 +52,9 @@ constexpr float kTileSumLimit = 256.0f;
 // K/V tile geometry per head dim.  At D = 128 a tile holds 32 keys: the
 // smaller score block and LDS footprint let three workgroups share a CU (at
 // most 168 registers per lane, 48 KB of LDS each), one more than 64-key tiles
-// allow there.  LDS holds two buffers of (K, V), each K tile followed by its
-// V tile; Q~ rows are staged after the first pair during the prologue.
+// allow there.  LDS holds buffer pairs of (K, V), each K tile followed by its
+// V tile (two pairs, or three for 32-key tiles); Q~ rows are staged after the
+// first pair during the prologue.
 template <int D>
 struct FwdTile {
   static constexpr int BN = D == 128 ? 32 : 64;  // keys per tile
